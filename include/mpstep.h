@@ -1,0 +1,240 @@
+/*
+ * mpstep -- the mixed-precision optimizer step on AMD Instinct MI355X (gfx950).
+ *
+ * One logical update of a mixed-precision training run, entirely on the GPU
+ * and stream-ordered (no host synchronisation on the hot path):
+ *
+ *   for each micro-batch i:  mp_accumulate        acc += (n_i/N) * widen(g16_i)
+ *   mp_unscale_check_norm                         g = acc / S, overflow flag,
+ *                                                 global L2 norm, clip coefficient
+ *   mp_adamw_step                                 AdamW on fp32 master, m, v;
+ *                                                 RNE cast master -> 16-bit weight;
+ *                                                 nothing is written on overflow
+ *   mp_scaler_update                              dynamic loss-scale decision
+ *
+ * The method is the one described on these pages (cited by title and section):
+ *  - "Mixed precision, loss scaling, gradient accumulation, and activation
+ *    checkpointing", section 2 "Principles" (16-bit formats, fp32 masters,
+ *    loss scaling, dynamic scaling, gradient accumulation) and section 4
+ *    "The interface" (scaler, grad_accumulate, train_step_mixed);
+ *  - "Megatron Internals III: Mixed Precision, Loss Scaling, and Grad
+ *    Clipping", sections 4-9 (unscale, controller, global overflow decision,
+ *    optimizer wrapper, fused gradient copy, global-norm clipping and the
+ *    order of operations);
+ *  - "Accumulate gradients and recompute activations", section "Weight each
+ *    mean by the targets it represents" (token-weighted accumulation) and
+ *    "Discard a failed partial logical update" (what a skip preserves);
+ *  - "Your weights fit on one device but Adam's moments do not", section "Why
+ *    the optimizer state is the thing that overflows" (the Adam update);
+ *  - "Chapter 41 Training at Scale", section 41.1, equation (41.1) (memory).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named in a plan or gradset are device pointers into memory the
+ *    CALLER owns (e.g. PyTorch allocations).  The library never frees them;
+ *    they must stay valid until the stream work that uses them has finished.
+ *    Every such pointer must be 16-byte aligned.
+ *  - The library owns plans, gradsets and states.  It allocates device memory
+ *    only in the *_create calls, never in the hot calls.
+ *  - Objects are bound to the HIP device that was current at creation; make it
+ *    current before calling a hot entry point.
+ *  - `stream` is a hipStream_t passed as void* (NULL: the null stream).  Hot
+ *    calls only enqueue work on it and return; results reach the host through
+ *    mp_state_read.
+ *  - Structural errors (bad arguments, wrong call order) are returned before
+ *    anything is enqueued.  Numeric overflow is NOT an error: it is a device
+ *    flag and the update is skipped on the device.
+ *  - A plan and a state are used by one stream at a time (not thread-safe).
+ */
+#ifndef MPSTEP_H
+#define MPSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MPSTEP_ABI_VERSION 1
+
+typedef enum {
+    MP_OK = 0,
+    MP_ERR_INVALID = 1,   /* an argument is out of range or NULL */
+    MP_ERR_ALIGN = 2,     /* a buffer is not 16-byte aligned */
+    MP_ERR_NOMEM = 3,     /* a device or host allocation failed */
+    MP_ERR_HIP = 4,       /* the HIP runtime reported an error */
+    MP_ERR_ORDER = 5      /* calls out of the documented order */
+} mp_status;
+
+/* The 16-bit model format ("Mixed precision ...", section 2, "Two 16-bit
+ * formats"): bf16 = 8 significant bits and fp32's exponent range; fp16 = 11
+ * significant bits, largest finite 65504, smallest subnormal 2^-24. */
+typedef enum { MP_BF16 = 0, MP_FP16 = 1 } mp_dtype16;
+
+typedef struct mp_plan mp_plan;        /* tensor list + chunk table (device) */
+typedef struct mp_gradset mp_gradset;  /* one micro-batch's gradient pointers (device) */
+typedef struct mp_state mp_state;      /* loss scale, optimizer clock, step results (device) */
+typedef void* mp_stream;               /* hipStream_t */
+
+/* Dynamic loss scaler ("Mixed precision ...", section 2 "Dynamic scaling";
+ * "Megatron Internals III", section 5).  init_scale, growth, backoff,
+ * min_scale and max_scale must be positive powers of two with growth >= 1,
+ * backoff <= 1 and min_scale <= init_scale <= max_scale; interval >= 1.
+ * enabled = 0 keeps S fixed at init_scale (bf16 needs no scaler). */
+typedef struct {
+    float init_scale;
+    float growth;
+    float backoff;
+    float min_scale;
+    float max_scale;
+    int32_t interval;
+    int32_t enabled;
+} mp_scaler_cfg;
+
+/* AdamW hyper-parameters: lr >= 0, 0 <= beta1, beta2 < 1, eps > 0,
+ * weight_decay >= 0 (all finite). */
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+} mp_adamw_hparams;
+
+/* What the device knows after a step (read with mp_state_read). */
+typedef struct {
+    int32_t found_inf;      /* the last unscale/check saw an inf or NaN */
+    int32_t skipped;        /* the last scaler update recorded a skipped step */
+    int32_t good_steps;     /* clean steps since the scale last changed */
+    int32_t reserved0;
+    int64_t step;           /* committed optimizer steps t */
+    int64_t skipped_total;  /* skipped steps so far */
+    double sumsq;           /* sum of squares of the unscaled gradient (fp64) */
+    double beta1_pow;       /* beta1^t */
+    double beta2_pow;       /* beta2^t */
+    float scale;            /* the loss scale S the next step uses */
+    float grad_norm;        /* fp32(sqrt(sumsq)) */
+    float clip_coef;        /* min(1, max_norm / (grad_norm + 1e-6)), or 1 */
+    float reserved1;
+} mp_stats;
+
+/* Human-readable name of a status code (static storage). */
+const char* mp_status_string(mp_status status);
+
+/* Detail of the last error returned to the calling thread ("" if none). */
+const char* mp_last_error(void);
+
+int32_t mp_abi_version(void);
+
+/* Token weights ("Accumulate gradients and recompute activations", "Weight
+ * each mean by the targets it represents"; counts validated as in "Extend the
+ * existing update and reverse owners"): weights_out[i] = fp32(n_i / N) with
+ * N = sum of counts, computed in binary64 then rounded once.  Host-only.
+ * MP_ERR_INVALID if k < 1, any n_i <= 0, or N > 2^53. */
+mp_status mp_token_weights(int32_t k, const int64_t* counts, float* weights_out);
+
+/* Model-state bytes per parameter ("Chapter 41 Training at Scale", equation
+ * (41.1)): 16-bit weight 2 + 16-bit gradient 2 + fp32 master 4 + m 4 + v 4 =
+ * 16, plus 4 for the fp32 accumulation buffer when with_accumulator != 0.
+ * The 16-bit weight and gradient are 2 bytes in both formats. */
+size_t mp_state_bytes_per_param(mp_dtype16 dtype, int32_t with_accumulator);
+
+/* Describe the parameter tensors of one model.  For tensor i (numel[i] >= 1
+ * elements, contiguous): acc[i] fp32 accumulation buffer, master[i] fp32
+ * master weight, m[i] and v[i] fp32 Adam moments, w16[i] the 16-bit model
+ * weight.  `acc` may be NULL when the model is never accumulated (one
+ * micro-batch per update: pass it as the last micro-batch with
+ * last_is_first = 1).  wd_mult[i] >= 0 multiplies weight_decay for tensor i
+ * (NULL: all 1).  Builds the chunk table and uploads it (synchronously).
+ * On success *out owns device memory until mp_plan_destroy. */
+mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dtype,
+                         void* const* acc, void* const* master, void* const* m,
+                         void* const* v, void* const* w16, const float* wd_mult,
+                         mp_plan** out);
+mp_status mp_plan_destroy(mp_plan* plan);
+
+/* Tensor and chunk counts of a plan (any output may be NULL). */
+mp_status mp_plan_info(const mp_plan* plan, int32_t* n_tensors, int64_t* total_params,
+                       int64_t* n_chunks, int32_t* chunk_elems);
+
+/* One micro-batch's 16-bit gradients: g16[i] points at numel[i] elements of
+ * the plan's 16-bit format, in the caller's device memory.  The pointer list
+ * is uploaded once (synchronously), so a gradset can be reused every step. */
+mp_status mp_gradset_create(const mp_plan* plan, void* const* g16, mp_gradset** out);
+mp_status mp_gradset_destroy(mp_gradset* set);
+
+/* Device state: S = init_scale, no good steps, t = 0, beta powers 1. */
+mp_status mp_state_create(const mp_scaler_cfg* cfg, mp_state** out);
+mp_status mp_state_destroy(mp_state* state);
+
+/* Enqueue a copy of the state into *out (host memory; pinned memory keeps the
+ * call asynchronous).  *out is valid once `stream` has reached this point. */
+mp_status mp_state_read(const mp_state* state, mp_stats* out, mp_stream stream);
+
+/* Device address of S (fp32), so the caller can scale its loss on the device
+ * ("Megatron Internals III", section 4: scaled_loss = S * loss). */
+mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale);
+
+/* Accumulate one micro-batch ("Mixed precision ...", section 2 "Gradient
+ * accumulation"; "Megatron Internals III", section 8): for every element,
+ *   first != 0:  acc = fl(weight * widen(g16))
+ *   first == 0:  acc = fl(acc + fl(weight * widen(g16)))
+ * where widen is the exact 16-bit -> fp32 conversion and weight = n_i/N from
+ * mp_token_weights (finite, > 0).  `first` starts a new logical update and
+ * discards whatever the buffer held (the gradients of a skipped step).
+ * MP_ERR_INVALID if the plan has no accumulators. */
+mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
+                        mp_stream stream);
+
+/* Unscale, check and measure ("Megatron Internals III", sections 4, 6 and 9;
+ * "Mixed precision ...", section 2 "Dynamic scaling").  The gradient of each
+ * element is g_eff = acc (last == NULL), fl(w_last * widen(last))
+ * (last_is_first != 0), or fl(acc + fl(w_last * widen(last))) -- the last
+ * micro-batch folded in exactly as mp_accumulate would add it.  Then
+ *   g = fl(g_eff * (1/S));  found_inf = any g is inf or NaN;
+ *   sumsq = sum g^2 in binary64 (fixed-order two-stage reduction, the same
+ *           bits on every run);  grad_norm = fp32(sqrt(sumsq));
+ *   clip_coef = min(1, fl(max_norm / fl(grad_norm + 1e-6))) if max_norm > 0
+ *               and !found_inf, else 1.
+ * Results stay on the device for mp_adamw_step and mp_state_read. */
+mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                                float w_last, int32_t last_is_first, float max_norm,
+                                mp_stream stream);
+
+/* AdamW + RNE cast ("Your weights fit on one device...", the Adam update;
+ * "Accumulate gradients...", decoupled decay; "Mixed precision ...", section 2
+ * "Why the weights stay float32"; "Megatron Internals III", section 9 steps
+ * 5-7).  Must follow mp_unscale_check_norm on the same plan and state with the
+ * same last/w_last/last_is_first (else MP_ERR_ORDER).  If found_inf: nothing
+ * is written and t, beta powers stay (the skipped step of "Discard a failed
+ * partial logical update").  Otherwise, with t' = t + 1, p_j = beta_j^t',
+ * bc_j = fp32(1 - p_j), scale = fl((1/S) * clip_coef), lambda = weight_decay
+ * * wd_mult[tensor], every element takes, each operation rounded to fp32:
+ *   gs = g_eff*scale;  m = b1*m + (1-b1)*gs;  v = b2*v + (1-b2)*(gs*gs);
+ *   u = (m/bc1) / (sqrt(v/bc2) + eps);  w = w - lr*(u + lambda*w);
+ *   w16 = round-to-nearest-even(w) in the plan's 16-bit format
+ * (NaN -> the format's quiet NaN with the sign kept). */
+mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                        int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream);
+
+/* Loss-scale decision after the step ("Mixed precision ...", section 2
+ * "Dynamic scaling"; "Megatron Internals III", section 5): skipped = found_inf;
+ * on overflow S = max(S*backoff, min_scale) and the count restarts; on a clean
+ * step the count grows and, on reaching `interval`, S = min(S*growth,
+ * max_scale) and the count restarts.  A disabled scaler keeps S. */
+mp_status mp_scaler_update(mp_state* state, mp_stream stream);
+
+/* Elementwise casts with the step's conversions: dst = round-to-nearest-even
+ * of src into the 16-bit format (as in mp_adamw_step), and dst = exact fp32
+ * value of a 16-bit pattern (as in mp_accumulate).  Useful to initialise the
+ * 16-bit weights from the masters.  n >= 0; buffers 16-byte aligned. */
+mp_status mp_cast_to_16(const float* src, uint16_t* dst, int64_t n, mp_dtype16 dtype,
+                        mp_stream stream);
+mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dtype,
+                      mp_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPSTEP_H */

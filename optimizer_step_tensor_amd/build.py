@@ -1,0 +1,32 @@
+"""Build libmpstep.so (the HIP kernels and the C ABI of include/mpstep.h) for gfx950."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libmpstep.so")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "kernels.hip")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -ffp-contract=off: no fusing of a*b+c, every operation rounds as written.
+# -fhip-fp32-correctly-rounded-divide-sqrt: IEEE division and square root.
+# -packed-fp32-ops off: no v_pk_* fp32 instructions are generated.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+         "-fno-gpu-flush-denormals-to-zero",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wextra", "-Wno-unused-parameter",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build(out=LIB, extra=()):
+    """Compile the library (always recompiles); returns its path."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,481 @@
+// C-ABI layer of the mixed-precision update step: argument validation, plan and
+// chunk-table construction, device state management and kernel launches.
+// Every entry point is declared and documented in include/mpstep.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using mpk::Chunk;
+using mpk::DevState;
+using mpk::TensorDesc;
+
+struct mp_plan {
+    int device;
+    int32_t n_tensors;
+    int32_t dtype;
+    bool has_acc;
+    int64_t total;
+    int64_t n_chunks;
+    int32_t chunk_elems;
+    int grid;                 // blocks of every element pass
+    TensorDesc* d_tensors;
+    Chunk* d_chunks;
+    double* d_partials;       // grid entries
+    // call-order bookkeeping: mp_adamw_step must follow mp_unscale_check_norm
+    bool norm_pending;
+    const mp_state* norm_state;
+    const mp_gradset* norm_last;
+    float norm_w_last;
+    int32_t norm_last_is_first;
+};
+
+struct mp_gradset {
+    const mp_plan* plan;
+    uint16_t** d_ptrs;
+};
+
+struct mp_state {
+    int device;
+    DevState* d;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+mp_status fail(mp_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+mp_status ok()
+{
+    g_error.clear();
+    return MP_OK;
+}
+
+mp_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(MP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+bool is_pow2(float x)
+{
+    if (!(x > 0.0f) || !std::isfinite(x)) return false;
+    int e;
+    return std::frexp(x, &e) == 0.5f;
+}
+
+bool valid_dtype(int d)
+{
+    return d == MP_BF16 || d == MP_FP16;
+}
+
+// Blocks of an element pass: enough to fill every CU several times over,
+// never more than there are chunks.
+constexpr int kBlocksPerCU = 8;
+
+int device_cus(int device)
+{
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    return cus;
+}
+
+// Chunk size: a power-of-two multiple of one block pass, small enough that the
+// table has several chunks per block on small models, large enough that the
+// table stays small (16 B per chunk) on large ones.
+int32_t pick_chunk_elems(int64_t total, int grid_cap)
+{
+    int64_t target = total / (4ll * grid_cap);
+    int64_t ch = mpk::kBlockSlab;
+    while (ch < target && ch < (1ll << 16)) ch <<= 1;
+    return static_cast<int32_t>(ch);
+}
+
+template <class T>
+hipError_t upload(T** dst, const std::vector<T>& src)
+{
+    *dst = nullptr;
+    if (src.empty()) return hipSuccess;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), src.size() * sizeof(T));
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(*dst);
+        *dst = nullptr;
+    }
+    return e;
+}
+
+mpk::PlanView view(const mp_plan* p)
+{
+    return mpk::PlanView{p->d_tensors, p->d_chunks, p->n_chunks};
+}
+
+mp_status check_hparams(const mp_adamw_hparams* hp)
+{
+    if (hp == nullptr) return fail(MP_ERR_INVALID, "hparams is NULL");
+    if (!std::isfinite(hp->lr) || hp->lr < 0.0f) return fail(MP_ERR_INVALID, "lr must be finite and >= 0");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f)) return fail(MP_ERR_INVALID, "beta1 must be in [0, 1)");
+    if (!(hp->beta2 >= 0.0f && hp->beta2 < 1.0f)) return fail(MP_ERR_INVALID, "beta2 must be in [0, 1)");
+    if (!std::isfinite(hp->eps) || !(hp->eps > 0.0f)) return fail(MP_ERR_INVALID, "eps must be finite and > 0");
+    if (!std::isfinite(hp->weight_decay) || hp->weight_decay < 0.0f)
+        return fail(MP_ERR_INVALID, "weight_decay must be finite and >= 0");
+    return MP_OK;
+}
+
+int grad_mode(const mp_gradset* last, int32_t last_is_first)
+{
+    if (last == nullptr) return mpk::kAccOnly;
+    return last_is_first ? mpk::kLastOnly : mpk::kAccPlusLast;
+}
+
+mp_status check_last(const mp_plan* plan, const mp_gradset* last, float w_last,
+                     int32_t last_is_first)
+{
+    if (last != nullptr && last->plan != plan)
+        return fail(MP_ERR_INVALID, "gradset belongs to another plan");
+    if (last != nullptr && (!std::isfinite(w_last) || !(w_last > 0.0f)))
+        return fail(MP_ERR_INVALID, "w_last must be finite and > 0");
+    if (last == nullptr && last_is_first)
+        return fail(MP_ERR_INVALID, "last_is_first needs a gradset");
+    if (grad_mode(last, last_is_first) != mpk::kLastOnly && !plan->has_acc)
+        return fail(MP_ERR_INVALID, "the plan has no accumulators: pass the only micro-batch "
+                                    "as `last` with last_is_first = 1");
+    return MP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mp_status_string(mp_status status)
+{
+    switch (status) {
+    case MP_OK: return "MP_OK";
+    case MP_ERR_INVALID: return "MP_ERR_INVALID";
+    case MP_ERR_ALIGN: return "MP_ERR_ALIGN";
+    case MP_ERR_NOMEM: return "MP_ERR_NOMEM";
+    case MP_ERR_HIP: return "MP_ERR_HIP";
+    case MP_ERR_ORDER: return "MP_ERR_ORDER";
+    }
+    return "MP_ERR_UNKNOWN";
+}
+
+const char* mp_last_error(void)
+{
+    return g_error.c_str();
+}
+
+int32_t mp_abi_version(void)
+{
+    return MPSTEP_ABI_VERSION;
+}
+
+mp_status mp_token_weights(int32_t k, const int64_t* counts, float* weights_out)
+{
+    if (k < 1 || counts == nullptr || weights_out == nullptr)
+        return fail(MP_ERR_INVALID, "need k >= 1 counts and an output array");
+    const int64_t limit = int64_t(1) << 53;
+    int64_t total = 0;
+    for (int32_t i = 0; i < k; ++i) {
+        if (counts[i] <= 0) return fail(MP_ERR_INVALID, "micro-batch %d has no targets", i);
+        if (counts[i] > limit - total)
+            return fail(MP_ERR_INVALID, "total target count exceeds 2^53");
+        total += counts[i];
+    }
+    for (int32_t i = 0; i < k; ++i)
+        weights_out[i] = static_cast<float>(static_cast<double>(counts[i]) / static_cast<double>(total));
+    return ok();
+}
+
+size_t mp_state_bytes_per_param(mp_dtype16 dtype, int32_t with_accumulator)
+{
+    (void)dtype;  // both 16-bit formats take 2 bytes
+    const size_t model16 = 2, grad16 = 2, master = 4, m = 4, v = 4;
+    return model16 + grad16 + master + m + v + (with_accumulator ? 4 : 0);
+}
+
+mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dtype,
+                         void* const* acc, void* const* master, void* const* m, void* const* v,
+                         void* const* w16, const float* wd_mult, mp_plan** out)
+{
+    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (n_tensors < 1) return fail(MP_ERR_INVALID, "n_tensors must be >= 1");
+    if (!valid_dtype(dtype)) return fail(MP_ERR_INVALID, "unknown dtype %d", (int)dtype);
+    if (numel == nullptr || master == nullptr || m == nullptr || v == nullptr || w16 == nullptr)
+        return fail(MP_ERR_INVALID, "numel, master, m, v and w16 arrays are required");
+    std::vector<TensorDesc> tensors(n_tensors);
+    std::vector<Chunk> chunks;
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
+            return fail(MP_ERR_INVALID, "tensor %d: numel %lld out of range", i, (long long)numel[i]);
+        void* ptrs[5] = {acc ? acc[i] : nullptr, master[i], m[i], v[i], w16[i]};
+        for (int k = 0; k < 5; ++k) {
+            if (k == 0 && acc == nullptr) continue;
+            if (ptrs[k] == nullptr) return fail(MP_ERR_INVALID, "tensor %d: NULL buffer", i);
+            if (!aligned16(ptrs[k])) return fail(MP_ERR_ALIGN, "tensor %d: buffer not 16-byte aligned", i);
+        }
+        const float mult = wd_mult ? wd_mult[i] : 1.0f;
+        if (!std::isfinite(mult) || mult < 0.0f)
+            return fail(MP_ERR_INVALID, "tensor %d: wd_mult must be finite and >= 0", i);
+        tensors[i] = TensorDesc{static_cast<float*>(ptrs[0]), static_cast<float*>(ptrs[1]),
+                                static_cast<float*>(ptrs[2]), static_cast<float*>(ptrs[3]),
+                                static_cast<uint16_t*>(ptrs[4]), numel[i], mult, 0};
+        total += numel[i];
+    }
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const int grid_cap = device_cus(device) * kBlocksPerCU;
+    const int32_t ch = pick_chunk_elems(total, grid_cap);
+    for (int32_t i = 0; i < n_tensors; ++i)
+        for (int64_t s = 0; s < numel[i]; s += ch)
+            chunks.push_back(Chunk{i, static_cast<int32_t>(std::min<int64_t>(ch, numel[i] - s)), s});
+    mp_plan* p = new (std::nothrow) mp_plan();
+    if (p == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+    p->device = device;
+    p->n_tensors = n_tensors;
+    p->dtype = dtype;
+    p->has_acc = acc != nullptr;
+    p->total = total;
+    p->n_chunks = static_cast<int64_t>(chunks.size());
+    p->chunk_elems = ch;
+    p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
+    std::vector<double> zeros(p->grid, 0.0);
+    if ((e = upload(&p->d_tensors, tensors)) != hipSuccess ||
+        (e = upload(&p->d_chunks, chunks)) != hipSuccess ||
+        (e = upload(&p->d_partials, zeros)) != hipSuccess) {
+        mp_plan_destroy(p);
+        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
+                                        : hip_fail(e, "plan upload");
+    }
+    *out = p;
+    return ok();
+}
+
+mp_status mp_plan_destroy(mp_plan* plan)
+{
+    if (plan == nullptr) return ok();
+    (void)hipFree(plan->d_tensors);
+    (void)hipFree(plan->d_chunks);
+    (void)hipFree(plan->d_partials);
+    delete plan;
+    return ok();
+}
+
+mp_status mp_plan_info(const mp_plan* plan, int32_t* n_tensors, int64_t* total_params,
+                       int64_t* n_chunks, int32_t* chunk_elems)
+{
+    if (plan == nullptr) return fail(MP_ERR_INVALID, "plan is NULL");
+    if (n_tensors) *n_tensors = plan->n_tensors;
+    if (total_params) *total_params = plan->total;
+    if (n_chunks) *n_chunks = plan->n_chunks;
+    if (chunk_elems) *chunk_elems = plan->chunk_elems;
+    return ok();
+}
+
+mp_status mp_gradset_create(const mp_plan* plan, void* const* g16, mp_gradset** out)
+{
+    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and g16 are required");
+    std::vector<uint16_t*> ptrs(plan->n_tensors);
+    for (int32_t i = 0; i < plan->n_tensors; ++i) {
+        if (g16[i] == nullptr) return fail(MP_ERR_INVALID, "gradient %d is NULL", i);
+        if (!aligned16(g16[i])) return fail(MP_ERR_ALIGN, "gradient %d not 16-byte aligned", i);
+        ptrs[i] = static_cast<uint16_t*>(g16[i]);
+    }
+    mp_gradset* g = new (std::nothrow) mp_gradset();
+    if (g == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+    g->plan = plan;
+    hipError_t e = upload(&g->d_ptrs, ptrs);
+    if (e != hipSuccess) {
+        delete g;
+        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
+                                        : hip_fail(e, "gradset upload");
+    }
+    *out = g;
+    return ok();
+}
+
+mp_status mp_gradset_destroy(mp_gradset* set)
+{
+    if (set == nullptr) return ok();
+    (void)hipFree(set->d_ptrs);
+    delete set;
+    return ok();
+}
+
+mp_status mp_state_create(const mp_scaler_cfg* cfg, mp_state** out)
+{
+    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (cfg == nullptr) return fail(MP_ERR_INVALID, "cfg is NULL");
+    if (!is_pow2(cfg->init_scale) || !is_pow2(cfg->growth) || !is_pow2(cfg->backoff) ||
+        !is_pow2(cfg->min_scale) || !is_pow2(cfg->max_scale))
+        return fail(MP_ERR_INVALID, "scales, growth and backoff must be positive powers of two");
+    if (cfg->growth < 1.0f || cfg->backoff > 1.0f)
+        return fail(MP_ERR_INVALID, "need growth >= 1 and backoff <= 1");
+    if (!(cfg->min_scale <= cfg->init_scale && cfg->init_scale <= cfg->max_scale))
+        return fail(MP_ERR_INVALID, "need min_scale <= init_scale <= max_scale");
+    if (cfg->interval < 1) return fail(MP_ERR_INVALID, "interval must be >= 1");
+    DevState h;
+    std::memset(&h, 0, sizeof h);
+    h.s.scale = cfg->init_scale;
+    h.s.beta1_pow = 1.0;
+    h.s.beta2_pow = 1.0;
+    h.s.clip_coef = 1.0f;
+    h.inv_scale = 1.0f / cfg->init_scale;
+    h.update_scale = h.inv_scale;
+    h.growth = cfg->growth;
+    h.backoff = cfg->backoff;
+    h.min_scale = cfg->min_scale;
+    h.max_scale = cfg->max_scale;
+    h.interval = cfg->interval;
+    h.enabled = cfg->enabled ? 1 : 0;
+    mp_state* s = new (std::nothrow) mp_state();
+    if (s == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+    hipError_t e = hipGetDevice(&s->device);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&s->d), sizeof(DevState));
+    if (e == hipSuccess) e = hipMemcpy(s->d, &h, sizeof h, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(s->d);
+        delete s;
+        return hip_fail(e, "state allocation");
+    }
+    *out = s;
+    return ok();
+}
+
+mp_status mp_state_destroy(mp_state* state)
+{
+    if (state == nullptr) return ok();
+    (void)hipFree(state->d);
+    delete state;
+    return ok();
+}
+
+mp_status mp_state_read(const mp_state* state, mp_stats* out, mp_stream stream)
+{
+    if (state == nullptr || out == nullptr) return fail(MP_ERR_INVALID, "state and out are required");
+    hipError_t e = hipMemcpyAsync(out, &state->d->s, sizeof(mp_stats), hipMemcpyDeviceToHost,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    return ok();
+}
+
+mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale)
+{
+    if (state == nullptr || dev_scale == nullptr) return fail(MP_ERR_INVALID, "state and out are required");
+    *dev_scale = &state->d->s.scale;
+    return ok();
+}
+
+mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
+                        mp_stream stream)
+{
+    if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and gradset are required");
+    if (g16->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
+    if (!plan->has_acc) return fail(MP_ERR_INVALID, "the plan has no accumulators");
+    if (!std::isfinite(weight) || !(weight > 0.0f)) return fail(MP_ERR_INVALID, "weight must be finite and > 0");
+    hipError_t e = mpk::launch_accumulate(view(plan), plan->grid, g16->d_ptrs, weight, first != 0,
+                                          plan->dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+    return ok();
+}
+
+mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                                float w_last, int32_t last_is_first, float max_norm,
+                                mp_stream stream)
+{
+    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
+    mp_status st = check_last(plan, last, w_last, last_is_first);
+    if (st != MP_OK) return st;
+    if (std::isnan(max_norm) || std::isinf(max_norm)) return fail(MP_ERR_INVALID, "max_norm must be finite");
+    hipError_t e = mpk::launch_norm(view(plan), plan->grid, last ? last->d_ptrs : nullptr, w_last,
+                                    grad_mode(last, last_is_first), plan->dtype, plan->d_partials,
+                                    max_norm, state->d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "norm launch");
+    plan->norm_pending = true;
+    plan->norm_state = state;
+    plan->norm_last = last;
+    plan->norm_w_last = w_last;
+    plan->norm_last_is_first = last_is_first ? 1 : 0;
+    return ok();
+}
+
+mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                        int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
+{
+    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
+    mp_status st = check_hparams(hp);
+    if (st != MP_OK) return st;
+    st = check_last(plan, last, w_last, last_is_first);
+    if (st != MP_OK) return st;
+    if (!plan->norm_pending || plan->norm_state != state || plan->norm_last != last ||
+        (last != nullptr && (plan->norm_w_last != w_last ||
+                             plan->norm_last_is_first != (last_is_first ? 1 : 0))))
+        return fail(MP_ERR_ORDER, "mp_adamw_step must follow mp_unscale_check_norm on the same "
+                                  "plan and state, with the same last micro-batch arguments");
+    mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    hipError_t e = mpk::launch_adamw(view(plan), plan->grid, last ? last->d_ptrs : nullptr, w_last,
+                                     grad_mode(last, last_is_first), plan->dtype, a, state->d,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "adamw launch");
+    plan->norm_pending = false;
+    return ok();
+}
+
+mp_status mp_scaler_update(mp_state* state, mp_stream stream)
+{
+    if (state == nullptr) return fail(MP_ERR_INVALID, "state is NULL");
+    hipError_t e = mpk::launch_scaler(state->d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "scaler launch");
+    return ok();
+}
+
+mp_status mp_cast_to_16(const float* src, uint16_t* dst, int64_t n, mp_dtype16 dtype,
+                        mp_stream stream)
+{
+    if (n < 0 || !valid_dtype(dtype)) return fail(MP_ERR_INVALID, "n must be >= 0, dtype known");
+    if (n > 0 && (src == nullptr || dst == nullptr)) return fail(MP_ERR_INVALID, "NULL buffer");
+    if (!aligned16(src) || !aligned16(dst)) return fail(MP_ERR_ALIGN, "buffers must be 16-byte aligned");
+    hipError_t e = mpk::launch_cast_to_16(src, dst, n, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cast launch");
+    return ok();
+}
+
+mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dtype,
+                      mp_stream stream)
+{
+    if (n < 0 || !valid_dtype(dtype)) return fail(MP_ERR_INVALID, "n must be >= 0, dtype known");
+    if (n > 0 && (src == nullptr || dst == nullptr)) return fail(MP_ERR_INVALID, "NULL buffer");
+    if (!aligned16(src) || !aligned16(dst)) return fail(MP_ERR_ALIGN, "buffers must be 16-byte aligned");
+    hipError_t e = mpk::launch_widen_16(src, dst, n, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "widen launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal layout shared by the C-ABI layer (api.hip) and the kernels (kernels.hip).
+//
+// Device-resident tables of one plan:
+//   TensorDesc[n_tensors]  -- the caller's buffers of each parameter tensor
+//   Chunk[n_chunks]        -- contiguous element ranges of at most chunk_elems
+//                             elements, never crossing a tensor; every element of
+//                             every tensor lies in exactly one chunk
+//   double[grid]           -- per-block partial sums of squares of the norm pass
+// A gradset is a device array uint16_t*[n_tensors].
+// The state is one DevState (the public mp_stats first, so mp_state_read copies
+// a prefix).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mpstep.h"
+
+namespace mpk {
+
+constexpr int kBlock = 256;                          // 4 wavefronts of 64 lanes
+constexpr int kWave = 64;
+constexpr int kGroup = 4;                            // elements per 16-byte fp32 vector
+constexpr int kGroupsPerLane = 2;                    // 8 elements per lane per pass
+constexpr int kWaveSlab = kWave * kGroup * kGroupsPerLane;   // 512 elements per wave pass
+constexpr int kBlockSlab = kBlock * kGroup * kGroupsPerLane; // 2048 elements per block pass
+
+struct TensorDesc {
+    float* acc;
+    float* master;
+    float* m;
+    float* v;
+    uint16_t* w16;
+    int64_t numel;
+    float wd_mult;
+    int32_t reserved;
+};
+
+struct Chunk {
+    int32_t tensor;
+    int32_t len;      // 1 .. chunk_elems
+    int64_t start;    // element offset inside the tensor, a multiple of kBlockSlab
+};
+
+struct DevState {
+    mp_stats s;             // public part (mp_state_read copies this prefix)
+    float inv_scale;        // 1/S (exact: S is a power of two)
+    float update_scale;     // fl(inv_scale * clip_coef), set by the norm pass
+    float growth, backoff, min_scale, max_scale;
+    int32_t interval;
+    int32_t enabled;
+};
+
+struct PlanView {
+    const TensorDesc* tensors;
+    const Chunk* chunks;
+    int64_t n_chunks;
+};
+
+struct AdamArgs {
+    float lr, beta1, beta2, eps, weight_decay;
+};
+
+// How the gradient of one element is formed (see mp_unscale_check_norm).
+enum GradMode { kAccOnly = 0, kLastOnly = 1, kAccPlusLast = 2 };
+
+hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, float w,
+                             int first, int dtype, hipStream_t s);
+hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+                       int mode, int dtype, double* partials, float max_norm, DevState* st,
+                       hipStream_t s);
+hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+                        int mode, int dtype, const AdamArgs& a, DevState* st, hipStream_t s);
+hipError_t launch_scaler(DevState* st, hipStream_t s);
+hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s);
+hipError_t launch_widen_16(const uint16_t* src, float* dst, int64_t n, int dtype, hipStream_t s);
+
+}  // namespace mpk

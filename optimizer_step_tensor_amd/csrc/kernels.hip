@@ -1,0 +1,535 @@
+// HIP kernels of the mixed-precision update step, written for CDNA4 (gfx950).
+//
+// All element passes share one layout: a block of 256 lanes (4 wave64s) walks
+// its chunks of the plan's chunk table; within a chunk each pass covers 2048
+// elements, each wave a contiguous 512-element slab, and each lane two groups
+// of 4 consecutive elements 256 elements apart, so every fp32 load or store
+// instruction of a wave moves one contiguous 1 KiB line run (16 B per lane)
+// and every 16-bit one a contiguous 512 B run.  Only the last partial group
+// of a tensor takes the scalar path.  Blocks take chunks b, b+G, b+2G, ... so
+// the assignment of elements to lanes is fixed, which makes the norm's
+// reduction order -- and its bits -- the same on every run.
+//
+// Arithmetic: compiled with -ffp-contract=off and correctly rounded fp32
+// division and square root, so every operation below is one IEEE-754 binary32
+// (or binary64) round-to-nearest-even step, in the order written.
+#include <type_traits>
+
+#include "internal.h"
+
+namespace mpk {
+namespace {
+
+// ---------------------------------------------------------------------------
+// 16-bit formats ("Mixed precision, loss scaling, gradient accumulation, and
+// activation checkpointing", section 2 "Two 16-bit formats").
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float widen16(uint32_t h);
+
+template <>
+__device__ __forceinline__ float widen16<MP_BF16>(uint32_t h)
+{
+    return __uint_as_float(h << 16);                     // bf16 is the top half of fp32
+}
+
+template <>
+__device__ __forceinline__ float widen16<MP_FP16>(uint32_t h)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// Round to nearest, ties to even.  NaN -> the format's quiet NaN, sign kept.
+template <int DT>
+__device__ __forceinline__ uint32_t round16(float x);
+
+template <>
+__device__ __forceinline__ uint32_t round16<MP_BF16>(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    // Adding 0x7FFF plus the lowest kept bit carries into the kept half exactly
+    // when the dropped half is above one half, or equal to it with an odd kept
+    // half; a carry out of the largest finite value lands on infinity.
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <>
+__device__ __forceinline__ uint32_t round16<MP_FP16>(float x)
+{
+    if (x != x) return ((__float_as_uint(x) >> 16) & 0x8000u) | 0x7E00u;
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));   // v_cvt_f16_f32, RNE
+}
+
+// ---------------------------------------------------------------------------
+// Memory access.  Pointers are cast to the global address space so the
+// compiler emits global_load/global_store (not flat) instructions; full groups
+// move 16 bytes (fp32) or 8 bytes (16-bit) per lane in one instruction.
+// nv = number of valid elements of a group (<= 0: none, >= 4: all).
+// ---------------------------------------------------------------------------
+#define MPK_GLOBAL __attribute__((address_space(1)))
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct F4 {
+    float v[4];
+};
+
+struct H4 {
+    uint32_t v[4];
+};
+
+template <bool FULL>
+__device__ __forceinline__ F4 load_f4(const float* p, int nv)
+{
+    F4 r;
+    if (FULL || nv >= kGroup) {
+        const f32x4 t = *(const MPK_GLOBAL f32x4*)(p);
+        r.v[0] = t.x; r.v[1] = t.y; r.v[2] = t.z; r.v[3] = t.w;
+    } else {
+        const MPK_GLOBAL float* g = (const MPK_GLOBAL float*)(p);
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) r.v[k] = k < nv ? g[k] : 0.0f;
+    }
+    return r;
+}
+
+template <bool FULL>
+__device__ __forceinline__ void store_f4(float* p, const F4& r, int nv)
+{
+    if (FULL || nv >= kGroup) {
+        f32x4 t;
+        t.x = r.v[0]; t.y = r.v[1]; t.z = r.v[2]; t.w = r.v[3];
+        *(MPK_GLOBAL f32x4*)(p) = t;
+    } else {
+        MPK_GLOBAL float* g = (MPK_GLOBAL float*)(p);
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k)
+            if (k < nv) g[k] = r.v[k];
+    }
+}
+
+template <bool FULL>
+__device__ __forceinline__ H4 load_h4(const uint16_t* p, int nv)
+{
+    H4 r;
+    if (FULL || nv >= kGroup) {
+        const u32x2 t = *(const MPK_GLOBAL u32x2*)(p);
+        r.v[0] = t.x & 0xFFFFu; r.v[1] = t.x >> 16; r.v[2] = t.y & 0xFFFFu; r.v[3] = t.y >> 16;
+    } else {
+        const MPK_GLOBAL uint16_t* g = (const MPK_GLOBAL uint16_t*)(p);
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) r.v[k] = k < nv ? static_cast<uint32_t>(g[k]) : 0u;
+    }
+    return r;
+}
+
+template <bool FULL>
+__device__ __forceinline__ void store_h4(uint16_t* p, const H4& r, int nv)
+{
+    if (FULL || nv >= kGroup) {
+        u32x2 t;
+        t.x = r.v[0] | (r.v[1] << 16);
+        t.y = r.v[2] | (r.v[3] << 16);
+        *(MPK_GLOBAL u32x2*)(p) = t;
+    } else {
+        MPK_GLOBAL uint16_t* g = (MPK_GLOBAL uint16_t*)(p);
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k)
+            if (k < nv) g[k] = static_cast<uint16_t>(r.v[k]);
+    }
+}
+
+// Run pass(full, base) over a chunk of `len` elements: every complete
+// 2048-element block pass with full = true_type (no bounds checks at all),
+// then the one partial pass, if any, with full = false_type.
+template <class Pass>
+__device__ __forceinline__ void for_each_pass(int len, Pass&& pass)
+{
+    int base = 0;
+    for (; base + kBlockSlab <= len; base += kBlockSlab) pass(std::true_type{}, base);
+    if (base < len) pass(std::false_type{}, base);
+}
+
+// Element offset of group h of this lane inside one 2048-element block pass.
+__device__ __forceinline__ int lane_offset(int h)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    return wave * kWaveSlab + h * (kWave * kGroup) + lane * kGroup;
+}
+
+__device__ __forceinline__ int valid_count(int len, int e)
+{
+    int r = len - e;
+    return r > kGroup ? kGroup : r;
+}
+
+// The fp32 gradient of one element ("Megatron Internals III", section 8;
+// "Mixed precision ...", section 2 "Gradient accumulation"): the accumulated
+// buffer, the last micro-batch alone, or the last micro-batch added to the
+// buffer with the same two roundings mp_accumulate uses.
+template <int DT, int MODE>
+__device__ __forceinline__ float grad_eff(float acc, uint32_t h, float w_last)
+{
+    if (MODE == kAccOnly) return acc;
+    const float contribution = w_last * widen16<DT>(h);
+    if (MODE == kLastOnly) return contribution;
+    return acc + contribution;
+}
+
+// Deterministic block sum of one double per lane (result valid in lane 0).
+__device__ __forceinline__ double block_sum(double x)
+{
+    __shared__ double wave_sums[kBlock / kWave];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) wave_sums[threadIdx.x / kWave] = x;
+    __syncthreads();
+    double total = 0.0;
+    if (threadIdx.x == 0) {
+        total = wave_sums[0];
+#pragma unroll
+        for (int w = 1; w < kBlock / kWave; ++w) total += wave_sums[w];
+    }
+    return total;
+}
+
+// ---------------------------------------------------------------------------
+// Accumulation of one micro-batch.
+// ---------------------------------------------------------------------------
+template <int DT, bool FIRST>
+__global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
+                                                       const uint16_t* const* __restrict__ g16,
+                                                       float w)
+{
+    for (int64_t c = blockIdx.x; c < p.n_chunks; c += gridDim.x) {
+        const Chunk ch = p.chunks[c];
+        float* acc = p.tensors[ch.tensor].acc + ch.start;
+        const uint16_t* g = g16[ch.tensor] + ch.start;
+        for_each_pass(ch.len, [&](auto full, int base) {
+            constexpr bool F = decltype(full)::value;
+            int e[kGroupsPerLane], nv[kGroupsPerLane];
+            H4 h[kGroupsPerLane];
+            F4 a[kGroupsPerLane];
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
+                e[j] = base + lane_offset(j);
+                nv[j] = F ? kGroup : valid_count(ch.len, e[j]);
+                h[j] = load_h4<F>(g + e[j], nv[j]);
+                if (!FIRST) a[j] = load_f4<F>(acc + e[j], nv[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
+                F4 out;
+#pragma unroll
+                for (int k = 0; k < kGroup; ++k) {
+                    const float contribution = w * widen16<DT>(h[j].v[k]);
+                    out.v[k] = FIRST ? contribution : a[j].v[k] + contribution;
+                }
+                store_f4<F>(acc + e[j], out, nv[j]);
+            }
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Unscale + sum of squares, first stage: one binary64 partial per block.
+// An inf or NaN gradient makes the sum inf or NaN; finite fp32 squares cannot
+// overflow binary64 for any element count a device can hold, so the overflow
+// flag is exactly "the sum is not finite".
+// ---------------------------------------------------------------------------
+template <int DT, int MODE>
+__global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
+                                                         const uint16_t* const* __restrict__ last,
+                                                         float w_last,
+                                                         const DevState* __restrict__ st,
+                                                         double* __restrict__ partials)
+{
+    const float inv = st->inv_scale;
+    double s = 0.0;
+    for (int64_t c = blockIdx.x; c < p.n_chunks; c += gridDim.x) {
+        const Chunk ch = p.chunks[c];
+        const float* acc = MODE == kLastOnly ? nullptr : p.tensors[ch.tensor].acc + ch.start;
+        const uint16_t* g = MODE == kAccOnly ? nullptr : last[ch.tensor] + ch.start;
+        for_each_pass(ch.len, [&](auto full, int base) {
+            constexpr bool F = decltype(full)::value;
+            int nv[kGroupsPerLane];
+            F4 a[kGroupsPerLane];
+            H4 h[kGroupsPerLane];
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
+                const int e = base + lane_offset(j);
+                nv[j] = F ? kGroup : valid_count(ch.len, e);
+                if (MODE != kLastOnly) a[j] = load_f4<F>(acc + e, nv[j]);
+                if (MODE != kAccOnly) h[j] = load_h4<F>(g + e, nv[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
+#pragma unroll
+                for (int k = 0; k < kGroup; ++k) {
+                    const float gv = grad_eff<DT, MODE>(MODE == kLastOnly ? 0.0f : a[j].v[k],
+                                                        MODE == kAccOnly ? 0u : h[j].v[k],
+                                                        w_last) * inv;
+                    const double d = static_cast<double>(gv);
+                    // the square of an fp32 value is exact in binary64, so this
+                    // fma is the same as a rounded add of the exact square; the
+                    // zeros loaded for elements past the tail add exactly 0
+                    s = __builtin_fma(d, d, s);
+                }
+            }
+        });
+    }
+    const double total = block_sum(s);
+    if (threadIdx.x == 0) partials[blockIdx.x] = total;
+}
+
+// Second stage: fixed-order sum of the partials, norm, clip coefficient
+// ("Megatron Internals III", section 9).
+__global__ __launch_bounds__(kBlock) void k_norm_finish(const double* __restrict__ partials,
+                                                        int n, float max_norm,
+                                                        DevState* __restrict__ st)
+{
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += kBlock) s += partials[i];
+    const double total = block_sum(s);
+    if (threadIdx.x == 0) {
+        const int found_inf = !__builtin_isfinite(total);
+        const float norm = static_cast<float>(__builtin_sqrt(total));
+        float coef = 1.0f;
+        if (max_norm > 0.0f && !found_inf) {
+            const float q = max_norm / (norm + 1e-6f);
+            coef = q < 1.0f ? q : 1.0f;
+        }
+        st->s.found_inf = found_inf;
+        st->s.sumsq = total;
+        st->s.grad_norm = norm;
+        st->s.clip_coef = coef;
+        st->update_scale = st->inv_scale * coef;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// AdamW on fp32 master/m/v and the RNE cast to the 16-bit weight.
+// ---------------------------------------------------------------------------
+template <int DT, int MODE>
+__global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
+                                                  const uint16_t* const* __restrict__ last,
+                                                  float w_last, AdamArgs a,
+                                                  const DevState* __restrict__ st)
+{
+    if (st->s.found_inf) return;                  // skipped step: write nothing
+    const float scale = st->update_scale;
+    const float bc1 = static_cast<float>(1.0 - st->s.beta1_pow * static_cast<double>(a.beta1));
+    const float bc2 = static_cast<float>(1.0 - st->s.beta2_pow * static_cast<double>(a.beta2));
+    const float b1 = a.beta1, b2 = a.beta2;
+    const float ob1 = 1.0f - b1, ob2 = 1.0f - b2;
+    const float eps = a.eps, lr = a.lr;
+    for (int64_t c = blockIdx.x; c < p.n_chunks; c += gridDim.x) {
+        const Chunk ch = p.chunks[c];
+        const TensorDesc td = p.tensors[ch.tensor];
+        const float lam = a.weight_decay * td.wd_mult;
+        const float* acc = MODE == kLastOnly ? nullptr : td.acc + ch.start;
+        const uint16_t* g = MODE == kAccOnly ? nullptr : last[ch.tensor] + ch.start;
+        float* mw = td.master + ch.start;
+        float* mm = td.m + ch.start;
+        float* mv = td.v + ch.start;
+        uint16_t* w16 = td.w16 + ch.start;
+        for_each_pass(ch.len, [&](auto full, int base) {
+            constexpr bool F = decltype(full)::value;
+            int e[kGroupsPerLane], nv[kGroupsPerLane];
+            F4 ga[kGroupsPerLane], wv[kGroupsPerLane], m[kGroupsPerLane], v[kGroupsPerLane];
+            H4 h[kGroupsPerLane];
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
+                e[j] = base + lane_offset(j);
+                nv[j] = F ? kGroup : valid_count(ch.len, e[j]);
+                if (MODE != kLastOnly) ga[j] = load_f4<F>(acc + e[j], nv[j]);
+                if (MODE != kAccOnly) h[j] = load_h4<F>(g + e[j], nv[j]);
+                wv[j] = load_f4<F>(mw + e[j], nv[j]);
+                m[j] = load_f4<F>(mm + e[j], nv[j]);
+                v[j] = load_f4<F>(mv + e[j], nv[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
+                H4 out16;
+#pragma unroll
+                for (int k = 0; k < kGroup; ++k) {
+                    const float gr = grad_eff<DT, MODE>(MODE == kLastOnly ? 0.0f : ga[j].v[k],
+                                                        MODE == kAccOnly ? 0u : h[j].v[k], w_last);
+                    const float gs = gr * scale;
+                    const float mj = b1 * m[j].v[k] + ob1 * gs;
+                    const float vj = b2 * v[j].v[k] + ob2 * (gs * gs);
+                    const float mh = mj / bc1;
+                    const float vh = vj / bc2;
+                    const float den = __builtin_sqrtf(vh) + eps;
+                    const float u = mh / den;
+                    float w = wv[j].v[k];
+                    w = w - lr * (u + lam * w);
+                    m[j].v[k] = mj;
+                    v[j].v[k] = vj;
+                    wv[j].v[k] = w;
+                    out16.v[k] = round16<DT>(w);
+                }
+                store_f4<F>(mw + e[j], wv[j], nv[j]);
+                store_f4<F>(mm + e[j], m[j], nv[j]);
+                store_f4<F>(mv + e[j], v[j], nv[j]);
+                store_h4<F>(w16 + e[j], out16, nv[j]);
+            }
+        });
+    }
+}
+
+// The optimizer clock advances only on a committed step ("Accumulate gradients
+// and recompute activations", "Discard a failed partial logical update").
+__global__ void k_adam_clock(DevState* __restrict__ st, float beta1, float beta2)
+{
+    if (threadIdx.x != 0 || st->s.found_inf) return;
+    st->s.step += 1;
+    st->s.beta1_pow = st->s.beta1_pow * static_cast<double>(beta1);
+    st->s.beta2_pow = st->s.beta2_pow * static_cast<double>(beta2);
+}
+
+// Dynamic loss-scale controller ("Mixed precision ...", section 2 "Dynamic
+// scaling"; "Megatron Internals III", section 5).
+__global__ void k_scaler(DevState* __restrict__ st)
+{
+    if (threadIdx.x != 0) return;
+    const int found_inf = st->s.found_inf;
+    st->s.skipped = found_inf;
+    if (found_inf) st->s.skipped_total += 1;
+    if (!st->enabled) return;
+    float scale = st->s.scale;
+    if (found_inf) {
+        const float next = scale * st->backoff;
+        scale = next > st->min_scale ? next : st->min_scale;
+        st->s.good_steps = 0;
+    } else {
+        int good = st->s.good_steps + 1;
+        if (good == st->interval) {
+            const float next = scale * st->growth;
+            scale = next < st->max_scale ? next : st->max_scale;
+            good = 0;
+        }
+        st->s.good_steps = good;
+    }
+    st->s.scale = scale;
+    st->inv_scale = 1.0f / scale;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_cast_to_16(const float* __restrict__ src,
+                                                       uint16_t* __restrict__ dst, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride)
+        dst[i] = static_cast<uint16_t>(round16<DT>(src[i]));
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_widen_16(const uint16_t* __restrict__ src,
+                                                     float* __restrict__ dst, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride)
+        dst[i] = widen16<DT>(src[i]);
+}
+
+unsigned elementwise_grid(int64_t n)
+{
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 8192) blocks = 8192;
+    return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
+}
+
+template <int DT, int MODE>
+void launch_norm_t(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+                   double* partials, DevState* st, hipStream_t s)
+{
+    k_norm_partial<DT, MODE><<<grid, kBlock, 0, s>>>(p, last, w_last, st, partials);
+}
+
+template <int DT, int MODE>
+void launch_adamw_t(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+                    const AdamArgs& a, DevState* st, hipStream_t s)
+{
+    k_adamw<DT, MODE><<<grid, kBlock, 0, s>>>(p, last, w_last, a, st);
+}
+
+}  // namespace
+
+hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, float w,
+                             int first, int dtype, hipStream_t s)
+{
+    if (dtype == MP_BF16) {
+        if (first) k_accumulate<MP_BF16, true><<<grid, kBlock, 0, s>>>(p, g16, w);
+        else       k_accumulate<MP_BF16, false><<<grid, kBlock, 0, s>>>(p, g16, w);
+    } else {
+        if (first) k_accumulate<MP_FP16, true><<<grid, kBlock, 0, s>>>(p, g16, w);
+        else       k_accumulate<MP_FP16, false><<<grid, kBlock, 0, s>>>(p, g16, w);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+                       int mode, int dtype, double* partials, float max_norm, DevState* st,
+                       hipStream_t s)
+{
+    if (dtype == MP_BF16) {
+        if (mode == kAccOnly)       launch_norm_t<MP_BF16, kAccOnly>(p, grid, last, w_last, partials, st, s);
+        else if (mode == kLastOnly) launch_norm_t<MP_BF16, kLastOnly>(p, grid, last, w_last, partials, st, s);
+        else                        launch_norm_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, partials, st, s);
+    } else {
+        if (mode == kAccOnly)       launch_norm_t<MP_FP16, kAccOnly>(p, grid, last, w_last, partials, st, s);
+        else if (mode == kLastOnly) launch_norm_t<MP_FP16, kLastOnly>(p, grid, last, w_last, partials, st, s);
+        else                        launch_norm_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, partials, st, s);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k_norm_finish<<<1, kBlock, 0, s>>>(partials, grid, max_norm, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+                        int mode, int dtype, const AdamArgs& a, DevState* st, hipStream_t s)
+{
+    if (dtype == MP_BF16) {
+        if (mode == kAccOnly)       launch_adamw_t<MP_BF16, kAccOnly>(p, grid, last, w_last, a, st, s);
+        else if (mode == kLastOnly) launch_adamw_t<MP_BF16, kLastOnly>(p, grid, last, w_last, a, st, s);
+        else                        launch_adamw_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, a, st, s);
+    } else {
+        if (mode == kAccOnly)       launch_adamw_t<MP_FP16, kAccOnly>(p, grid, last, w_last, a, st, s);
+        else if (mode == kLastOnly) launch_adamw_t<MP_FP16, kLastOnly>(p, grid, last, w_last, a, st, s);
+        else                        launch_adamw_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, a, st, s);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k_adam_clock<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
+    return hipGetLastError();
+}
+
+hipError_t launch_scaler(DevState* st, hipStream_t s)
+{
+    k_scaler<<<1, 64, 0, s>>>(st);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    if (dtype == MP_BF16) k_cast_to_16<MP_BF16><<<elementwise_grid(n), kBlock, 0, s>>>(src, dst, n);
+    else                  k_cast_to_16<MP_FP16><<<elementwise_grid(n), kBlock, 0, s>>>(src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_widen_16(const uint16_t* src, float* dst, int64_t n, int dtype, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    if (dtype == MP_BF16) k_widen_16<MP_BF16><<<elementwise_grid(n), kBlock, 0, s>>>(src, dst, n);
+    else                  k_widen_16<MP_FP16><<<elementwise_grid(n), kBlock, 0, s>>>(src, dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace mpk

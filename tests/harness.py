@@ -1,0 +1,207 @@
+"""Drivers that run one workload through the HIP library and through the oracle.
+
+Both sides read the same seeded inputs (``inputs``): the device side fills its
+buffers with the generator's HIP twin, the oracle side with its host twin.
+Nothing flows from the HIP path into the oracle.  The update schedule is the
+same on both sides: micro-batches 1..k-1 accumulated, the last one folded into
+the norm and update passes.
+"""
+import numpy as np
+
+import inputs
+import oracle
+from inputs import configs
+
+
+def oracle_dtype(w):
+    return oracle.BF16 if w.dtype == inputs.BF16 else oracle.FP16
+
+
+INF16 = {inputs.BF16: 0x7F80, inputs.FP16: 0x7C00}
+
+
+class OracleRun:
+    """The workload on host arrays, stepped by the oracle."""
+
+    def __init__(self, w, threads=8):
+        self.w = w
+        dt = oracle_dtype(w)
+        masters = [inputs.gen_host_f32(n, w.master_recipe(t)) for t, n in enumerate(w.numels)]
+        w16 = [oracle.rd16(x, dt) for x in masters]
+        sc = (oracle.make_scaler(**w.scaler) if w.scaler is not None
+              else oracle.make_scaler(init_scale=1.0, enabled=False))
+        self.st = oracle.OracleStep(dt, masters, w16, scaler=sc, with_acc=w.k > 1,
+                                    threads=threads)
+        self.step_no = 0
+
+    def grads(self, step, micro):
+        S = self.st.scaler.scale
+        g = [inputs.gen_host_u16(n, self.w.grad_recipe(step, micro, t, S), self.w.dtype)
+             for t, n in enumerate(self.w.numels)]
+        if micro == self.w.k - 1:
+            inj = self.w.injection(step)
+            if inj is not None:
+                g[inj[0]][inj[1]] = INF16[self.w.dtype]
+        return g
+
+    def step(self):
+        """One logical update; returns the accumulator snapshot before the fold (or None)."""
+        self.step_no += 1
+        w, st, s = self.w, self.st, self.step_no
+        self.prev_master = [x.copy() for x in st.masters]
+        self.prev_m = [x.copy() for x in st.m]
+        weights = oracle.token_weights(w.token_counts(s))
+        for i in range(w.k - 1):
+            st.accumulate(self.grads(s, i), weights[i], i == 0)
+        acc_snapshot = [a.copy() for a in st.acc] if st.acc is not None else None
+        last = self.grads(s, w.k - 1)
+        lif = w.k == 1
+        st.unscale_check_norm(last, weights[-1], lif, w.max_norm)
+        st.adamw_step(last, weights[-1], lif, **w.hp)
+        st.scaler_update()
+        return acc_snapshot
+
+
+class DeviceRun:
+    """The workload in device buffers, stepped by libmpstep."""
+
+    def __init__(self, w, sep_grads=True):
+        import torch
+        import optimizer_step_tensor_amd as mp
+        self.torch, self.mp, self.w = torch, mp, w
+        dt = mp.MP_BF16 if w.dtype == inputs.BF16 else mp.MP_FP16
+        self.model = mp.ModelState(w.numels, dt, with_acc=w.k > 1)
+        for t, x in enumerate(self.model.master):
+            inputs.fill_dev_f32(x, w.master_recipe(t))
+        for x, y in zip(self.model.master, self.model.w16):
+            mp.mp_cast_to_16(x.data_ptr(), y.data_ptr(), x.numel(), dt)
+        t16 = torch.bfloat16 if w.dtype == inputs.BF16 else torch.float16
+        n_sets = w.k if sep_grads else 1
+        self.g16 = [[torch.empty(n, dtype=t16, device="cuda") for n in w.numels]
+                    for _ in range(n_sets)]
+        self.gsets = [self.model.gradset(g) for g in self.g16]
+        cfg = (mp.scaler_cfg(**w.scaler) if w.scaler is not None
+               else mp.scaler_cfg(init_scale=1.0, enabled=False))
+        self.state = mp.mp_state_create(cfg)
+        self.hp = mp.adamw_hparams(**w.hp)
+        self.step_no = 0
+
+    def stats(self):
+        return self.mp.read_stats(self.state)
+
+    def fill_grads(self, step, scale):
+        """Generate every micro-batch's gradients of `step` (with the given loss scale)."""
+        w = self.w
+        for i in range(w.k):
+            gl = self.g16[i % len(self.g16)]
+            for t, x in enumerate(gl):
+                inputs.fill_dev_u16(x, w.grad_recipe(step, i, t, scale), w.dtype)
+            if i == w.k - 1:
+                inj = w.injection(step)
+                if inj is not None:
+                    gl[inj[0]].view(self.torch.int16)[inj[1]] = INF16[w.dtype]
+
+    def step(self, scale, snapshot=False):
+        """One logical update with inputs generated at loss scale `scale`."""
+        self.step_no += 1
+        mp, w, s = self.mp, self.w, self.step_no
+        assert len(self.g16) == w.k, "per-micro-batch buffers needed to run a step"
+        self.fill_grads(s, scale)
+        weights = mp.mp_token_weights(w.token_counts(s))
+        for i in range(w.k - 1):
+            mp.mp_accumulate(self.model.plan, self.gsets[i], weights[i], i == 0)
+        acc_snapshot = ([a.cpu().numpy() for a in self.model.acc]
+                        if snapshot and self.model.acc is not None else None)
+        last, lif = self.gsets[w.k - 1], w.k == 1
+        mp.mp_unscale_check_norm(self.model.plan, self.state, last, weights[-1], lif, w.max_norm)
+        mp.mp_adamw_step(self.model.plan, self.state, last, weights[-1], lif, self.hp)
+        mp.mp_scaler_update(self.state)
+        return acc_snapshot
+
+    def host(self, name):
+        bufs = getattr(self.model, name)
+        out = []
+        for b in bufs:
+            a = b.cpu()
+            if a.dtype in (self.torch.bfloat16, self.torch.float16):
+                a = a.view(self.torch.int16).numpy().view(np.uint16)
+            else:
+                a = a.numpy()
+            out.append(a)
+        return out
+
+    def close(self):
+        for g in self.gsets:
+            self.mp.mp_gradset_destroy(g)
+        self.mp.mp_state_destroy(self.state)
+        self.model.close()
+
+
+def rel_within(x, r, bound):
+    """|x - r| <= bound elementwise (all arrays float64)."""
+    return np.abs(x.astype(np.float64) - r.astype(np.float64)) <= bound
+
+
+def compare_step(dev, orc, w, step, acc_dev=None, acc_orc=None):
+    """Compare the device state after a step with the oracle's.  Returns a report dict;
+    raises AssertionError on any violation of the parity bar."""
+    st = dev.stats()
+    o = orc.st
+    rep = {"step": step, "found_inf": st["found_inf"], "scale": st["scale"],
+           "norm_gpu": st["grad_norm"], "norm_oracle": o.norm}
+    # integer decisions: bit-exact
+    assert st["found_inf"] == int(o.found_inf), rep
+    assert st["skipped"] == o.scaler.skipped, rep
+    assert st["scale"] == o.scaler.scale, rep
+    assert st["good_steps"] == o.scaler.good_steps, rep
+    assert st["step"] == o.clock.t, rep
+    assert st["skipped_total"] == o.scaler.skipped_total, rep
+    assert st["beta1_pow"] == o.clock.p1 and st["beta2_pow"] == o.clock.p2, rep
+    if acc_dev is not None:
+        for a, b in zip(acc_dev, acc_orc):
+            fin = np.isfinite(b)
+            assert np.array_equal(a[fin].view(np.uint32), b[fin].view(np.uint32)), "acc bits"
+            assert np.array_equal(np.isfinite(a), fin), "acc non-finite pattern"
+    if o.found_inf:
+        assert not np.isfinite(st["sumsq"]), rep
+    else:
+        # norm: within 1e-5 relative of the oracle's compensated binary64 value
+        # (binary64 sums in two orders: far inside the 1e-5 bar of the norm)
+        assert abs(st["sumsq"] - o.sumsq) <= 1e-10 * o.sumsq + 1e-300, rep
+        assert abs(st["grad_norm"] - o.norm) <= 1e-5 * o.norm, rep
+        assert abs(st["clip_coef"] - o.coef) <= 1e-5 * o.coef, rep
+    # a skipped step writes nothing on either side: the state must stay bit-identical
+    same_norm = bool(o.found_inf) or (np.float32(st["grad_norm"]) == np.float32(o.norm)
+                                      and np.float32(st["clip_coef"]) == np.float32(o.coef))
+    rep["same_norm_bits"] = bool(same_norm)
+    masters, m, v, w16 = dev.host("master"), dev.host("m"), dev.host("v"), dev.host("w16")
+    dt = oracle_dtype(w)
+    mism = 0
+    for t in range(len(masters)):
+        # the 16-bit weight is the RNE cast of the device's own master, bit for bit
+        assert np.array_equal(w16[t], oracle.rd16(masters[t], dt)), "w16 != rd16(master)"
+        if same_norm:
+            for a, b, nm in ((masters[t], o.masters[t], "master"), (m[t], o.m[t], "m"),
+                             (v[t], o.v[t], "v"), (w16[t], o.w16[t], "w16")):
+                bad = a.view(a.dtype) != b
+                if bad.any():
+                    idx = int(np.flatnonzero(bad)[0])
+                    raise AssertionError("%s bits differ: tensor %d index %d gpu %r oracle %r"
+                                         % (nm, t, idx, a[idx], b[idx]))
+        else:
+            # tolerance of the parity bar: 2e-6 relative to the magnitude of the
+            # terms each value is made of (so cancellation near 0 is judged fairly)
+            rtol = 2e-6
+            b1 = np.float64(np.float32(w.hp["beta1"]))
+            lam = w.hp["lr"] * w.hp["weight_decay"]
+            r_v = o.v[t].astype(np.float64)
+            assert rel_within(v[t], r_v, rtol * np.abs(r_v) + 1e-45).all(), "v tolerance"
+            r_m, m0 = o.m[t].astype(np.float64), orc.prev_m[t].astype(np.float64)
+            bound_m = rtol * (b1 * np.abs(m0) + np.abs(r_m - b1 * m0)) + 1e-45
+            assert rel_within(m[t], r_m, bound_m).all(), "m tolerance"
+            r_w, w0 = o.masters[t].astype(np.float64), orc.prev_master[t].astype(np.float64)
+            bound_w = rtol * (np.abs(w0) * (1 + lam) + np.abs(w0 - r_w)) + 1e-45
+            assert rel_within(masters[t], r_w, bound_w).all(), "master tolerance"
+            mism += int((w16[t] != o.w16[t]).sum())
+    rep["w16_mismatch"] = mism
+    return rep

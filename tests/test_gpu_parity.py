@@ -1,0 +1,173 @@
+"""Parity of the HIP library with the oracle, element by element (needs an MI355X).
+
+Every call goes through the C ABI (the ctypes binding of include/mpstep.h).
+The bar: bit-exact for the 16-bit casts, the accumulation buffer, overflow
+flags, skip decisions, scaler state and optimizer clock; the global norm within
+1e-5 relative; masters and moments bit-exact whenever both sides' fp32 norms
+agree (else within 2e-6 relative to the magnitude of their terms).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import inputs  # noqa: E402
+import oracle  # noqa: E402
+from inputs import configs  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mp():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import optimizer_step_tensor_amd as m
+    m.lib()
+    return m
+
+
+def test_library_exports_and_device(mp):
+    import torch
+    say("device:", torch.cuda.get_device_name(0))
+    assert mp.mp_abi_version() == 1
+
+
+def test_widen_all_16bit_patterns(mp):
+    import torch
+    h = torch.arange(1 << 16, dtype=torch.int32, device="cuda").to(torch.int16)
+    out = torch.empty(1 << 16, dtype=torch.float32, device="cuda")
+    for dt in (mp.MP_BF16, mp.MP_FP16):
+        mp.mp_widen_16(h.data_ptr(), out.data_ptr(), 1 << 16, dt)
+        got = out.cpu().numpy()
+        ref = oracle.widen16(h.cpu().numpy().view(np.uint16), dt)
+        nan = np.isnan(ref)
+        assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+        assert np.isnan(got[nan]).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_round_all_fp32_patterns(mp, dtype):
+    """All 2^32 fp32 inputs: the device cast equals the oracle's rd16 bit for bit."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    dt = mp.MP_BF16 if dtype == "bf16" else mp.MP_FP16
+    chunk = 1 << 28
+    src = torch.empty(chunk, dtype=torch.int32, device="cuda")
+    dst = torch.empty(chunk, dtype=torch.int16, device="cuda")
+    L = oracle.lib()
+    bad = 0
+    for c in range((1 << 32) // chunk):
+        src.copy_(torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64,
+                               device="cuda").to(torch.int32))
+        mp.mp_cast_to_16(src.data_ptr(), dst.data_ptr(), chunk, dt)
+        got = dst.cpu().numpy().view(np.uint16)
+        x = src.cpu().numpy().view(np.float32)
+        parts = 16
+        step = chunk // parts
+
+        def ref(i):
+            return oracle.rd16(x[i * step:(i + 1) * step], dt, L)
+
+        with ThreadPoolExecutor(16) as ex:
+            want = np.concatenate(list(ex.map(ref, range(parts))))
+        bad += int((got != want).sum())
+        say("cast %s chunk %d/16 mismatches so far %d" % (dtype, c + 1, bad))
+    assert bad == 0
+
+
+def test_generator_twins_agree(mp):
+    """The device fill and the host fill of every recipe kind give the same bits."""
+    import torch
+    n, off = 100_003, 12_345
+    recs = [inputs.recipe(inputs.key(99, 1), inputs.NORMAL, sigma=0.02),
+            inputs.recipe(inputs.key(99, 2), inputs.NORMAL_TAIL, sigma=1e-4, tail_prob=0.01,
+                          tail_mult=100.0),
+            inputs.recipe(inputs.key(99, 3), inputs.LOGUNIF_MIX, sigma=1e-3, scale=2.0 ** 16,
+                          tail_prob=0.05, lo_exp=-30, hi_exp=-20)]
+    for r in recs:
+        d = torch.empty(n, dtype=torch.float32, device="cuda")
+        inputs.fill_dev_f32(d, r, off)
+        assert np.array_equal(d.cpu().numpy().view(np.uint32),
+                              inputs.gen_host_f32(n, r, off).view(np.uint32))
+        for dt in (inputs.BF16, inputs.FP16):
+            h = torch.empty(n, dtype=torch.int16, device="cuda")
+            inputs.fill_dev_u16(h, r, dt, off)
+            assert np.array_equal(h.cpu().numpy().view(np.uint16),
+                                  inputs.gen_host_u16(n, r, dt, off))
+
+
+PARITY = ["edges", "edges-fp16", "llama-10.5M", "gpt-124M", "gpt-1.3B-small",
+          "ragged-4096-small", "llama3-8B-small"]
+
+
+@pytest.mark.parametrize("name", PARITY)
+def test_workload_parity(mp, name):
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make(name)
+    say("workload %s: %d tensors, %d params, k=%d, %d steps"
+        % (name, len(w.tensors), w.total, w.k, w.steps))
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            acc_o = orc.step()
+            acc_d = dev.step(scale, snapshot=True)
+            rep = compare_step(dev, orc, w, s, acc_d, acc_o)
+            say("  step", s, rep)
+    finally:
+        dev.close()
+
+
+def test_norm_is_deterministic(mp):
+    """The same inputs give the same sum of squares, bit for bit, on every run."""
+    from harness import DeviceRun
+    w = configs.make("ragged-4096-small")
+    dev = DeviceRun(w)
+    try:
+        dev.fill_grads(1, 1.0)
+        sums = []
+        for _ in range(3):
+            mp.mp_unscale_check_norm(dev.model.plan, dev.state, dev.gsets[0], 0.25, 1, 1.0)
+            sums.append(dev.stats()["sumsq"])
+        assert sums[0] == sums[1] == sums[2]
+    finally:
+        dev.close()
+
+
+def test_call_order_and_argument_errors(mp):
+    """Structural errors are refused before anything is enqueued."""
+    from harness import DeviceRun
+    w = configs.make("edges")
+    dev = DeviceRun(w)
+    try:
+        plan, st, g = dev.model.plan, dev.state, dev.gsets[0]
+        with pytest.raises(mp.MpError) as e:
+            mp.mp_adamw_step(plan, st, None, 1.0, 0, dev.hp)
+        assert e.value.status == mp.MP_ERR_ORDER
+        mp.mp_unscale_check_norm(plan, st, g, 0.5, 0, 1.0)
+        with pytest.raises(mp.MpError) as e:           # different last micro-batch weight
+            mp.mp_adamw_step(plan, st, g, 0.25, 0, dev.hp)
+        assert e.value.status == mp.MP_ERR_ORDER
+        mp.mp_adamw_step(plan, st, g, 0.5, 0, dev.hp)
+        with pytest.raises(mp.MpError):                # nothing pending any more
+            mp.mp_adamw_step(plan, st, g, 0.5, 0, dev.hp)
+        for bad in (0.0, -1.0, float("nan"), float("inf")):
+            with pytest.raises(mp.MpError) as e:
+                mp.mp_accumulate(plan, g, bad, 1)
+            assert e.value.status == mp.MP_ERR_INVALID
+        hp = mp.adamw_hparams(beta1=1.0)
+        mp.mp_unscale_check_norm(plan, st, g, 0.5, 0, 1.0)
+        with pytest.raises(mp.MpError):
+            mp.mp_adamw_step(plan, st, g, 0.5, 0, hp)
+        with pytest.raises(mp.MpError) as e:
+            mp.mp_state_create(mp.scaler_cfg(init_scale=3.0))
+        assert e.value.status == mp.MP_ERR_INVALID
+    finally:
+        dev.close()
