@@ -1,0 +1,264 @@
+"""Throughput of the fused mixed-precision update step on one MI355X.
+
+One step = one logical update of the whole hot path over one batch of synthetic
+input: token weights, micro-batches 1..k-1 accumulated into the fp32 buffers,
+the last micro-batch folded into the unscale/overflow/norm pass and into the
+AdamW + RNE-cast pass, then the loss-scaler decision.  Inputs (fp32 masters,
+per-micro-batch bf16 gradients) are generated on the device before the timed
+region and stay resident in HBM.
+
+Prints ONE JSON line: params/s of the whole step (value), the roofline of the
+dominant kernel (the AdamW pass, timed live with HIP events on the stream it
+runs on), and the oracle timed on the host's cores over a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "fused mixed-precision step: params/sec and HBM GB/s (% of peak), 1 MI355X"
+KERNEL_SOURCES = [os.path.join(ROOT, "optimizer_step_tensor_amd", "csrc", f)
+                  for f in ("api.hip", "internal.h", "kernels.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-8B.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bytes_per_param(k):
+    """Algorithmic HBM bytes per parameter of each pass (16-bit = 2 B, fp32 = 4 B)."""
+    return {
+        "accumulate_first": 2 + 4,            # read g16, write acc
+        "accumulate": 2 + 4 + 4,              # read g16 + acc, write acc
+        "norm": 4 + 2,                        # read acc + last g16
+        # read acc (k > 1), last g16, w, m, v; write w, m, v, w16
+        "adamw": (4 if k > 1 else 0) + 2 + 4 + 4 + 4 + (4 + 4 + 4 + 2),
+        "step": (6 + 10 * (k - 2) + 6 + 32) if k >= 2 else (2 + 2 + 4 * 3 + 12 + 2),
+    }
+
+
+def cpu_baseline(w, seconds_hint=20.0):
+    """The oracle (as it stands) on a bounded sample: layer-0-sized tensors of the workload,
+    split into 16M-element segments so the host threads share the work."""
+    import numpy as np
+    import inputs
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    # sample: the tensors of the first transformer layer (after the embedding)
+    sample, total = [], 0
+    for t, n in enumerate(w.numels[1:], start=1):
+        sample.append((t, n))
+        total += n
+        if total >= 200_000_000 or len(sample) >= 9:
+            break
+    seg = 16 * 1024 * 1024
+    pieces = []
+    for t, n in sample:
+        for off in range(0, n, seg):
+            pieces.append((t, off, min(seg, n - off)))
+    dt = oracle.BF16
+    masters = [inputs.gen_host_f32(c, w.master_recipe(t), off) for t, off, c in pieces]
+    st = oracle.OracleStep(dt, masters, [np.zeros(x.size, np.uint16) for x in masters],
+                           with_acc=w.k > 1, threads=threads)
+    grads = [[inputs.gen_host_u16(c, w.grad_recipe(1, i, t), w.dtype, off)
+              for t, off, c in pieces] for i in range(w.k)]
+    weights = oracle.token_weights(w.token_counts(1))
+    t0 = time.perf_counter()
+    for i in range(w.k - 1):
+        st.accumulate(grads[i], weights[i], i == 0)
+    st.unscale_check_norm(grads[-1], weights[-1], w.k == 1, w.max_norm)
+    st.adamw_step(grads[-1], weights[-1], w.k == 1, **w.hp)
+    st.scaler_update()
+    dt_s = time.perf_counter() - t0
+    n_sample = sum(p[2] for p in pieces)
+    return {"value": n_sample / dt_s, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": "%d params (%d tensors of the first layer, %d segments), k=%d, one full step, "
+                      "%.1f s" % (n_sample, len(sample), len(pieces), w.k, dt_s)}
+
+
+def kernel_sha():
+    """Digest of the library sources: counter results are only reused for identical code."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per AdamW launch from the committed rocprofv3 counter runs, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3-8B")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 4 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import inputs
+    import optimizer_step_tensor_amd as mp
+    from inputs import configs
+
+    w = configs.make(args.workload)
+    P, k = w.total, w.k
+    log("workload %s: %d tensors, %d params, k=%d" % (w.name, len(w.tensors), P, k))
+    torch.cuda.set_device(0)
+    dt16 = mp.MP_BF16 if w.dtype == inputs.BF16 else mp.MP_FP16
+    t16 = torch.bfloat16 if w.dtype == inputs.BF16 else torch.float16
+    model = mp.ModelState(w.numels, dt16, with_acc=k > 1)
+    for t, x in enumerate(model.master):
+        inputs.fill_dev_f32(x, w.master_recipe(t))
+    for x, y in zip(model.master, model.w16):
+        mp.mp_cast_to_16(x.data_ptr(), y.data_ptr(), x.numel(), dt16)
+    cfg = (mp.scaler_cfg(**w.scaler) if w.scaler is not None
+           else mp.scaler_cfg(init_scale=1.0, enabled=False))
+    state = mp.mp_state_create(cfg)
+    S0 = cfg.init_scale
+    g16 = []
+    for i in range(k):
+        g16.append([torch.empty(n, dtype=t16, device="cuda") for n in w.numels])
+        for t, x in enumerate(g16[-1]):
+            inputs.fill_dev_u16(x, w.grad_recipe(1, i, t, S0), w.dtype)
+    sets = [model.gradset(g) for g in g16]
+    hp = mp.adamw_hparams(**w.hp)
+    weights = mp.mp_token_weights(w.token_counts(1))
+    plan = model.plan
+    stream = torch.cuda.current_stream()
+    info = mp.mp_plan_info(plan)
+    log("plan:", info, "| resident %.1f GB" % (torch.cuda.memory_allocated() / 1e9))
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read, %d bytes written" % (4 * n, 4 * n))
+        del a, b
+
+    ev = {name: [] for name in ("accumulate", "norm", "adamw")}
+
+    def one_step(record):
+        def timed(name, fn):
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[name].append((e0, e1))
+            else:
+                fn()
+        lif = k == 1
+        for i in range(k - 1):
+            timed("accumulate", lambda i=i: mp.mp_accumulate(plan, sets[i], weights[i], i == 0,
+                                                             stream))
+        timed("norm", lambda: mp.mp_unscale_check_norm(plan, state, sets[-1], weights[-1], lif,
+                                                       w.max_norm, stream))
+        timed("adamw", lambda: mp.mp_adamw_step(plan, state, sets[-1], weights[-1], lif, hp,
+                                                stream))
+        mp.mp_scaler_update(state, stream)
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        one_step(True)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = g0.elapsed_time(g1)
+    ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
+    stats = mp.read_stats(state)
+    log("stats after timing:", stats)
+
+    bpp = bytes_per_param(k)
+    kernel_ms = {n: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None)
+                 for n, v in ev.items()}
+    adam_bytes = bpp["adamw"] * P
+    achieved = adam_bytes / (kernel_ms["adamw"] * 1e-3) / 1e9
+    step_bytes = bpp["step"] * P
+    log("per-launch ms:", {n: round(x, 4) for n, x in kernel_ms.items() if x})
+    log("step: %.3f ms, %.1f GB/s algorithmic (%.1f%% of %.0f)"
+        % (ms_per_step, step_bytes / ms_per_step / 1e6, step_bytes / ms_per_step / 1e6 /
+           HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
+
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": P / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
+        "config": {"workload": w.name, "params": P, "tensors": len(w.tensors), "k": k,
+                   "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
+                   "schedule": "k-1 accumulate passes, last micro-batch folded into norm and "
+                               "AdamW passes",
+                   "step_bytes_per_param": bpp["step"],
+                   "step_GBps": step_bytes / ms_per_step / 1e6,
+                   "step_hbm_frac": step_bytes / ms_per_step / 1e6 / HBM_PEAK_GBPS,
+                   "kernel_ms": kernel_ms,
+                   "chunk_elems": info["chunk_elems"], "n_chunks": info["n_chunks"]},
+        "roofline": {"bound": "hbm", "kernel": "k_adamw (AdamW + RNE cast, last micro-batch "
+                                                "folded in)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "bytes_per_param": bpp["adamw"],
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    for s in sets:
+        mp.mp_gradset_destroy(s)
+    mp.mp_state_destroy(state)
+    model.close()
+    del g16, model
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on the host cores) ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

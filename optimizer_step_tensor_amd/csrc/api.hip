@@ -22,10 +22,11 @@ struct mp_plan {
     int64_t total;
     int64_t n_chunks;
     int32_t chunk_elems;
-    int grid;                 // blocks of every element pass
+    int grid;                 // blocks of the accumulate and AdamW passes
+    int norm_grid;            // blocks of the norm pass (= partial sums)
     TensorDesc* d_tensors;
     Chunk* d_chunks;
-    double* d_partials;       // grid entries
+    double* d_partials;       // norm_grid entries
     // call-order bookkeeping: mp_adamw_step must follow mp_unscale_check_norm
     bool norm_pending;
     const mp_state* norm_state;
@@ -87,9 +88,6 @@ bool valid_dtype(int d)
     return d == MP_BF16 || d == MP_FP16;
 }
 
-// Blocks of an element pass: enough to fill every CU several times over,
-// never more than there are chunks.
-constexpr int kBlocksPerCU = 8;
 
 int device_cus(int device)
 {
@@ -248,8 +246,10 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    const int grid_cap = device_cus(device) * kBlocksPerCU;
-    const int32_t ch = pick_chunk_elems(total, grid_cap);
+    const int cus = device_cus(device);
+    const int64_t grid_cap = MPK_ELEM_BLOCKS_PER_CU > 0 ? int64_t(cus) * MPK_ELEM_BLOCKS_PER_CU
+                                                         : int64_t(1) << 30;
+    const int32_t ch = pick_chunk_elems(total, cus * 8);
     for (int32_t i = 0; i < n_tensors; ++i)
         for (int64_t s = 0; s < numel[i]; s += ch)
             chunks.push_back(Chunk{i, static_cast<int32_t>(std::min<int64_t>(ch, numel[i] - s)), s});
@@ -263,7 +263,8 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
     p->n_chunks = static_cast<int64_t>(chunks.size());
     p->chunk_elems = ch;
     p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
-    std::vector<double> zeros(p->grid, 0.0);
+    p->norm_grid = static_cast<int>(std::min<int64_t>(p->n_chunks, cus * MPK_NORM_BLOCKS_PER_CU));
+    std::vector<double> zeros(p->norm_grid, 0.0);
     if ((e = upload(&p->d_tensors, tensors)) != hipSuccess ||
         (e = upload(&p->d_chunks, chunks)) != hipSuccess ||
         (e = upload(&p->d_partials, zeros)) != hipSuccess) {
@@ -414,7 +415,7 @@ mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset
     mp_status st = check_last(plan, last, w_last, last_is_first);
     if (st != MP_OK) return st;
     if (std::isnan(max_norm) || std::isinf(max_norm)) return fail(MP_ERR_INVALID, "max_norm must be finite");
-    hipError_t e = mpk::launch_norm(view(plan), plan->grid, last ? last->d_ptrs : nullptr, w_last,
+    hipError_t e = mpk::launch_norm(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr, w_last,
                                     grad_mode(last, last_is_first), plan->dtype, plan->d_partials,
                                     max_norm, state->d, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm launch");

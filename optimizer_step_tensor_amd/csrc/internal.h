@@ -18,10 +18,31 @@
 
 namespace mpk {
 
+// Launch shape (compile-time).  The defaults were chosen by timing variants on
+// MI355X with the 8B-parameter tensor list resident: one block per chunk for the
+// accumulate and AdamW passes (the dispatcher then balances ragged chunks), 32
+// blocks per CU for the norm pass, and the nontemporal hint on every streamed
+// load and store (each byte is touched once per pass).
+#ifndef MPK_GROUPS_PER_LANE
+#define MPK_GROUPS_PER_LANE 2      // groups of 4 elements per lane per block pass
+#endif
+#ifndef MPK_ELEM_BLOCKS_PER_CU
+#define MPK_ELEM_BLOCKS_PER_CU 0   // accumulate / AdamW grid cap per CU; 0: one block per chunk
+#endif
+#ifndef MPK_NORM_BLOCKS_PER_CU
+#define MPK_NORM_BLOCKS_PER_CU 32  // norm grid: blocks per compute unit (fixed per plan)
+#endif
+#ifndef MPK_NT_LOADS
+#define MPK_NT_LOADS 1             // nontemporal hint on streamed loads
+#endif
+#ifndef MPK_NT_STORES
+#define MPK_NT_STORES 1            // nontemporal hint on streamed stores
+#endif
+
 constexpr int kBlock = 256;                          // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
 constexpr int kGroup = 4;                            // elements per 16-byte fp32 vector
-constexpr int kGroupsPerLane = 2;                    // 8 elements per lane per pass
+constexpr int kGroupsPerLane = MPK_GROUPS_PER_LANE;
 constexpr int kWaveSlab = kWave * kGroup * kGroupsPerLane;   // 512 elements per wave pass
 constexpr int kBlockSlab = kBlock * kGroup * kGroupsPerLane; // 2048 elements per block pass
 

@@ -86,7 +86,8 @@ __device__ __forceinline__ F4 load_f4(const float* p, int nv)
 {
     F4 r;
     if (FULL || nv >= kGroup) {
-        const f32x4 t = *(const MPK_GLOBAL f32x4*)(p);
+        const MPK_GLOBAL f32x4* q = (const MPK_GLOBAL f32x4*)(p);
+        const f32x4 t = MPK_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
         r.v[0] = t.x; r.v[1] = t.y; r.v[2] = t.z; r.v[3] = t.w;
     } else {
         const MPK_GLOBAL float* g = (const MPK_GLOBAL float*)(p);
@@ -102,7 +103,9 @@ __device__ __forceinline__ void store_f4(float* p, const F4& r, int nv)
     if (FULL || nv >= kGroup) {
         f32x4 t;
         t.x = r.v[0]; t.y = r.v[1]; t.z = r.v[2]; t.w = r.v[3];
-        *(MPK_GLOBAL f32x4*)(p) = t;
+        MPK_GLOBAL f32x4* q = (MPK_GLOBAL f32x4*)(p);
+        if (MPK_NT_STORES) __builtin_nontemporal_store(t, q);
+        else *q = t;
     } else {
         MPK_GLOBAL float* g = (MPK_GLOBAL float*)(p);
 #pragma unroll
@@ -116,7 +119,8 @@ __device__ __forceinline__ H4 load_h4(const uint16_t* p, int nv)
 {
     H4 r;
     if (FULL || nv >= kGroup) {
-        const u32x2 t = *(const MPK_GLOBAL u32x2*)(p);
+        const MPK_GLOBAL u32x2* q = (const MPK_GLOBAL u32x2*)(p);
+        const u32x2 t = MPK_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
         r.v[0] = t.x & 0xFFFFu; r.v[1] = t.x >> 16; r.v[2] = t.y & 0xFFFFu; r.v[3] = t.y >> 16;
     } else {
         const MPK_GLOBAL uint16_t* g = (const MPK_GLOBAL uint16_t*)(p);
@@ -133,7 +137,9 @@ __device__ __forceinline__ void store_h4(uint16_t* p, const H4& r, int nv)
         u32x2 t;
         t.x = r.v[0] | (r.v[1] << 16);
         t.y = r.v[2] | (r.v[3] << 16);
-        *(MPK_GLOBAL u32x2*)(p) = t;
+        MPK_GLOBAL u32x2* q = (MPK_GLOBAL u32x2*)(p);
+        if (MPK_NT_STORES) __builtin_nontemporal_store(t, q);
+        else *q = t;
     } else {
         MPK_GLOBAL uint16_t* g = (MPK_GLOBAL uint16_t*)(p);
 #pragma unroll
