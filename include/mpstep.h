@@ -157,6 +157,16 @@ mp_status mp_plan_destroy(mp_plan* plan);
 mp_status mp_plan_info(const mp_plan* plan, int32_t* n_tensors, int64_t* total_params,
                        int64_t* n_chunks, int32_t* chunk_elems);
 
+/* The chunk table mp_plan_create builds for `numel` on a device with n_cus
+ * compute units, computed on the host (no device needed).  Every tensor is cut
+ * into contiguous chunks of at most *chunk_elems elements (a power-of-two
+ * multiple of 2048; the last chunk of a tensor is ragged), tensor by tensor.
+ * Writes *n_chunks and up to `capacity` entries of (tensor index, start
+ * element, length) into the optional output arrays. */
+mp_status mp_chunk_layout(int32_t n_tensors, const int64_t* numel, int32_t n_cus,
+                          int32_t* chunk_elems, int64_t* n_chunks, int32_t* tensor_out,
+                          int64_t* start_out, int32_t* len_out, int64_t capacity);
+
 /* One micro-batch's 16-bit gradients: g16[i] points at numel[i] elements of
  * the plan's 16-bit format, in the caller's device memory.  The pointer list
  * is uploaded once (synchronously), so a gradset can be reused every step. */

@@ -25,6 +25,7 @@ MP_OK, MP_ERR_INVALID, MP_ERR_ALIGN, MP_ERR_NOMEM, MP_ERR_HIP, MP_ERR_ORDER = ra
 ENTRY_POINTS = [
     "mp_status_string", "mp_last_error", "mp_abi_version", "mp_token_weights",
     "mp_state_bytes_per_param", "mp_plan_create", "mp_plan_destroy", "mp_plan_info",
+    "mp_chunk_layout",
     "mp_gradset_create", "mp_gradset_destroy", "mp_state_create", "mp_state_destroy",
     "mp_state_read", "mp_state_scale_ptr", "mp_accumulate", "mp_unscale_check_norm",
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
@@ -89,6 +90,7 @@ def _bind(L):
         "mp_plan_create": ([i32, P, i32, PP, PP, PP, PP, PP, P, PP], i32),
         "mp_plan_destroy": ([P], i32),
         "mp_plan_info": ([P, P, P, P, P], i32),
+        "mp_chunk_layout": ([i32, P, i32, P, P, P, P, P, i64], i32),
         "mp_gradset_create": ([P, PP, PP], i32),
         "mp_gradset_destroy": ([P], i32),
         "mp_state_create": ([ctypes.POINTER(ScalerCfg), PP], i32),
@@ -183,6 +185,20 @@ def mp_plan_info(plan):
                               ctypes.byref(ce)))
     return {"n_tensors": nt.value, "total_params": tot.value, "n_chunks": nc.value,
             "chunk_elems": ce.value}
+
+
+def mp_chunk_layout(numel, n_cus):
+    """(chunk_elems, [(tensor, start, len), ...]) of the plan mp_plan_create would build."""
+    n = len(numel)
+    ne = (ctypes.c_int64 * n)(*[int(x) for x in numel])
+    ce, nc = ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().mp_chunk_layout(n, ne, n_cus, ctypes.byref(ce), ctypes.byref(nc), None, None,
+                                 None, 0))
+    t = (ctypes.c_int32 * nc.value)()
+    s = (ctypes.c_int64 * nc.value)()
+    ln = (ctypes.c_int32 * nc.value)()
+    _check(lib().mp_chunk_layout(n, ne, n_cus, None, None, t, s, ln, nc.value))
+    return ce.value, list(zip(t, s, ln))
 
 
 def mp_gradset_create(plan, g16):

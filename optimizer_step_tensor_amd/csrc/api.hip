@@ -109,6 +109,20 @@ int32_t pick_chunk_elems(int64_t total, int grid_cap)
     return static_cast<int32_t>(ch);
 }
 
+// The chunk table of a tensor list: every tensor cut into ranges of at most
+// chunk_elems elements (the last one ragged), tensor by tensor, in order.
+int32_t build_chunks(int32_t n_tensors, const int64_t* numel, int cus, std::vector<Chunk>& chunks)
+{
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) total += numel[i];
+    const int32_t ch = pick_chunk_elems(total, cus * 8);
+    chunks.clear();
+    for (int32_t i = 0; i < n_tensors; ++i)
+        for (int64_t s = 0; s < numel[i]; s += ch)
+            chunks.push_back(Chunk{i, static_cast<int32_t>(std::min<int64_t>(ch, numel[i] - s)), s});
+    return ch;
+}
+
 template <class T>
 hipError_t upload(T** dst, const std::vector<T>& src)
 {
@@ -249,10 +263,7 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
     const int cus = device_cus(device);
     const int64_t grid_cap = MPK_ELEM_BLOCKS_PER_CU > 0 ? int64_t(cus) * MPK_ELEM_BLOCKS_PER_CU
                                                          : int64_t(1) << 30;
-    const int32_t ch = pick_chunk_elems(total, cus * 8);
-    for (int32_t i = 0; i < n_tensors; ++i)
-        for (int64_t s = 0; s < numel[i]; s += ch)
-            chunks.push_back(Chunk{i, static_cast<int32_t>(std::min<int64_t>(ch, numel[i] - s)), s});
+    const int32_t ch = build_chunks(n_tensors, numel, cus, chunks);
     mp_plan* p = new (std::nothrow) mp_plan();
     if (p == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
     p->device = device;
@@ -294,6 +305,28 @@ mp_status mp_plan_info(const mp_plan* plan, int32_t* n_tensors, int64_t* total_p
     if (total_params) *total_params = plan->total;
     if (n_chunks) *n_chunks = plan->n_chunks;
     if (chunk_elems) *chunk_elems = plan->chunk_elems;
+    return ok();
+}
+
+mp_status mp_chunk_layout(int32_t n_tensors, const int64_t* numel, int32_t n_cus,
+                          int32_t* chunk_elems, int64_t* n_chunks, int32_t* tensor_out,
+                          int64_t* start_out, int32_t* len_out, int64_t capacity)
+{
+    if (n_tensors < 1 || numel == nullptr || n_cus < 1)
+        return fail(MP_ERR_INVALID, "need n_tensors >= 1, numel and n_cus >= 1");
+    for (int32_t i = 0; i < n_tensors; ++i)
+        if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
+            return fail(MP_ERR_INVALID, "tensor %d: numel out of range", i);
+    std::vector<Chunk> chunks;
+    const int32_t ch = build_chunks(n_tensors, numel, n_cus, chunks);
+    if (chunk_elems) *chunk_elems = ch;
+    if (n_chunks) *n_chunks = static_cast<int64_t>(chunks.size());
+    const int64_t n = std::min<int64_t>(capacity, static_cast<int64_t>(chunks.size()));
+    for (int64_t c = 0; c < n; ++c) {
+        if (tensor_out) tensor_out[c] = chunks[c].tensor;
+        if (start_out) start_out[c] = chunks[c].start;
+        if (len_out) len_out[c] = chunks[c].len;
+    }
     return ok();
 }
 

@@ -1,0 +1,134 @@
+"""The C-ABI library on the host, without a GPU (CPU only).
+
+Checks that libmpstep.so loads and exports every entry point include/mpstep.h
+declares, and exercises the host-only logic: status strings, token weights,
+memory accounting, the chunk table, and argument validation that returns before
+any device work.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpstep.h")
+
+
+@pytest.fixture(scope="module")
+def mp():
+    import optimizer_step_tensor_amd as m
+    m.lib()
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported(mp):
+    names = declared_functions()
+    assert len(names) >= 20
+    raw = ctypes.CDLL(mp.build.LIB)
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert missing == []
+    assert sorted(mp.ENTRY_POINTS) == names
+
+
+def test_status_strings_and_version(mp):
+    assert mp.mp_abi_version() == 1
+    assert [mp.mp_status_string(s) for s in range(6)] == [
+        "MP_OK", "MP_ERR_INVALID", "MP_ERR_ALIGN", "MP_ERR_NOMEM", "MP_ERR_HIP", "MP_ERR_ORDER"]
+
+
+def test_token_weights_match_the_oracle(mp):
+    rng = np.random.default_rng(1)
+    for k in (1, 2, 3, 4, 8, 31):
+        counts = rng.integers(1, 10 ** 6, k)
+        assert np.array_equal(np.array(mp.mp_token_weights(counts), np.float32),
+                              oracle.token_weights(counts))
+    with pytest.raises(mp.MpError) as e:
+        mp.mp_token_weights([4, 0])
+    assert e.value.status == mp.MP_ERR_INVALID
+    with pytest.raises(mp.MpError):
+        mp.mp_token_weights([2 ** 53, 1])
+    with pytest.raises(mp.MpError):
+        mp.mp_token_weights([])
+
+
+def test_bytes_per_parameter(mp):
+    """'Chapter 41 Training at Scale' equation (41.1): 16 bytes, plus the fp32 accumulator."""
+    for dt in (mp.MP_BF16, mp.MP_FP16):
+        assert mp.mp_state_bytes_per_param(dt, False) == oracle.model_state_bytes(1) == 16
+        assert mp.mp_state_bytes_per_param(dt, True) == 20
+
+
+def _check_layout(mp, numel, cus):
+    ch, chunks = mp.mp_chunk_layout(numel, cus)
+    assert ch % 2048 == 0 and ch & (ch - 1) == 0 and 2048 <= ch <= 65536
+    covered = [0] * len(numel)
+    prev = (-1, -1)
+    for t, s, ln in chunks:
+        assert 1 <= ln <= ch
+        assert s % ch == 0                      # chunks start on chunk (hence vector) boundaries
+        assert s == covered[t]                  # contiguous, in order, no overlap or gap
+        assert (t, s) > prev
+        prev = (t, s)
+        covered[t] = s + ln
+    assert covered == list(numel)               # every element exactly once
+    return ch, chunks
+
+
+def test_chunk_layout_covers_every_element_once(mp):
+    from inputs import configs
+    for name in ("edges", "llama-10.5M", "gpt-124M", "ragged-4096-small", "llama3-8B"):
+        w = configs.make(name)
+        _check_layout(mp, w.numels, 256)
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        n = rng.integers(1, 200)
+        numel = list(rng.integers(1, 300_000, n))
+        _check_layout(mp, numel, int(rng.integers(1, 400)))
+
+
+def test_chunk_size_grows_with_the_model(mp):
+    small, _ = _check_layout(mp, [10_000], 256)
+    big, chunks = _check_layout(mp, [2 ** 33], 256)
+    assert small == 2048 and big == 65536 and len(chunks) == 2 ** 33 // 65536
+
+
+def test_validation_before_any_device_work(mp):
+    """Refusals that return before the library touches a device."""
+    L = mp.lib()
+    out = ctypes.c_void_p()
+    ne = (ctypes.c_int64 * 1)(16)
+    good = (ctypes.c_void_p * 1)(0x10000)
+    bad = (ctypes.c_void_p * 1)(0x10008)           # 8-byte aligned only
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    g = ctypes.cast(good, PP)
+    assert L.mp_plan_create(0, ne, 0, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert L.mp_plan_create(1, ne, 7, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert L.mp_plan_create(1, ne, 0, None, None, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert (L.mp_plan_create(1, ne, 0, None, ctypes.cast(bad, PP), g, g, g, None, ctypes.byref(out))
+            == mp.MP_ERR_ALIGN)
+    assert "aligned" in mp.mp_last_error()
+    zero = (ctypes.c_int64 * 1)(0)
+    assert L.mp_plan_create(1, zero, 0, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    neg = (ctypes.c_float * 1)(-1.0)
+    assert L.mp_plan_create(1, ne, 0, None, g, g, g, g, neg, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    for cfg in (mp.scaler_cfg(init_scale=3.0), mp.scaler_cfg(growth=0.5), mp.scaler_cfg(backoff=2.0),
+                mp.scaler_cfg(interval=0), mp.scaler_cfg(min_scale=2.0 ** 20),
+                mp.scaler_cfg(init_scale=float("inf"))):
+        assert L.mp_state_create(ctypes.byref(cfg), ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert L.mp_accumulate(None, None, 1.0, 1, None) == mp.MP_ERR_INVALID
+    assert L.mp_unscale_check_norm(None, None, None, 1.0, 0, 1.0, None) == mp.MP_ERR_INVALID
+    assert L.mp_scaler_update(None, None) == mp.MP_ERR_INVALID
+    assert L.mp_cast_to_16(None, None, -1, 0, None) == mp.MP_ERR_INVALID
+    assert L.mp_cast_to_16(ctypes.c_void_p(0x10004), ctypes.c_void_p(0x10000), 4, 0,
+                           None) == mp.MP_ERR_ALIGN
+    assert L.mp_cast_to_16(None, None, 0, 0, None) == mp.MP_OK      # empty cast: nothing to do
