@@ -46,8 +46,9 @@ def host():
             _build.build_host()
         L = ctypes.CDLL(_build.HOST_LIB)
         u64, i64, P = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
-        L.mpgen_fill_f32_host.argtypes = [P, i64, i64, ctypes.POINTER(Recipe)]
-        L.mpgen_fill_u16_host.argtypes = [P, i64, i64, ctypes.POINTER(Recipe), ctypes.c_int]
+        L.mpgen_fill_f32_host.argtypes = [P, i64, i64, ctypes.POINTER(Recipe), ctypes.c_int]
+        L.mpgen_fill_u16_host.argtypes = [P, i64, i64, ctypes.POINTER(Recipe), ctypes.c_int,
+                                          ctypes.c_int]
         L.mpgen_key_host.argtypes = [u64] * 5
         L.mpgen_key_host.restype = u64
         L.mpgen_draw_host.argtypes = [u64, u64]
@@ -89,24 +90,25 @@ def uniform(k, index):
     return host().mpgen_uniform_host(k, index)
 
 
-def fill_host_f32(out, r, offset=0):
+def fill_host_f32(out, r, offset=0, threads=0):
+    """Elements offset .. offset+n-1 of stream r (threads: 0 = OpenMP default, 1 = caller only)."""
     assert out.dtype == np.float32 and out.flags.c_contiguous
-    host().mpgen_fill_f32_host(out.ctypes.data, out.size, offset, ctypes.byref(r))
+    host().mpgen_fill_f32_host(out.ctypes.data, out.size, offset, ctypes.byref(r), threads)
     return out
 
 
-def fill_host_u16(out, r, dtype, offset=0):
+def fill_host_u16(out, r, dtype, offset=0, threads=0):
     assert out.dtype == np.uint16 and out.flags.c_contiguous
-    host().mpgen_fill_u16_host(out.ctypes.data, out.size, offset, ctypes.byref(r), dtype)
+    host().mpgen_fill_u16_host(out.ctypes.data, out.size, offset, ctypes.byref(r), dtype, threads)
     return out
 
 
-def gen_host_f32(n, r, offset=0):
-    return fill_host_f32(np.empty(n, np.float32), r, offset)
+def gen_host_f32(n, r, offset=0, threads=0):
+    return fill_host_f32(np.empty(n, np.float32), r, offset, threads)
 
 
-def gen_host_u16(n, r, dtype, offset=0):
-    return fill_host_u16(np.empty(n, np.uint16), r, dtype, offset)
+def gen_host_u16(n, r, dtype, offset=0, threads=0):
+    return fill_host_u16(np.empty(n, np.uint16), r, dtype, offset, threads)
 
 
 def fill_dev_f32(t, r, offset=0, stream=None):

@@ -154,6 +154,12 @@ def make(name):
         return Workload(17, name, [("f%02d" % i, (n,)) for i, n in enumerate(sizes)], FP16, 2,
                         grad_kind=LOGUNIF_MIX, tail_prob=0.05, lo_exp=-30, hi_exp=-20,
                         scaler=dict(FP16_SCALER, interval=2), inject_step=2, steps=6)
+    if name == "gpt-124M-scaler":
+        # the fp16 run's scaler, overflow and gradient recipe on a small tensor list, long enough
+        # for the scale to grow back: 2000 clean steps after the overflow of step 3
+        return Workload(18, name, [("a", (1000,)), ("b", (3001,)), ("c", (768,))], FP16, 1,
+                        grad_kind=LOGUNIF_MIX, tail_prob=0.05, lo_exp=-30, hi_exp=-20,
+                        scaler=dict(FP16_SCALER), inject_step=3, steps=2003)
     raise KeyError(name)
 
 

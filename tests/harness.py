@@ -205,3 +205,155 @@ def compare_step(dev, orc, w, step, acc_dev=None, acc_orc=None):
             mism += int((w16[t] != o.w16[t]).sum())
     rep["w16_mismatch"] = mism
     return rep
+
+
+class StreamedOracle:
+    """The oracle at full size, streamed: the global norm is recomputed every step from
+    regenerated inputs, segment by segment (memory bounded by the segment size), and
+    the update itself is computed on sampled windows only.  Each window's fp32 state
+    (master, m, v) is carried from step to step by the oracle itself."""
+
+    SEG = 1 << 24
+
+    def __init__(self, w, windows, threads=16, log=print, seg=None):
+        self.w, self.windows, self.threads, self.log = w, windows, threads, log
+        if seg is not None:
+            self.SEG = seg
+        self.dt = oracle_dtype(w)
+        self.scaler = (oracle.make_scaler(**w.scaler) if w.scaler is not None
+                       else oracle.make_scaler(init_scale=1.0, enabled=False))
+        self.clock = oracle.make_clock()
+        self.state = []
+        for t, start, n in windows:
+            master = inputs.gen_host_f32(n, w.master_recipe(t), start)
+            self.state.append({"master": master, "m": np.zeros(n, np.float32),
+                               "v": np.zeros(n, np.float32), "w16": oracle.rd16(master, self.dt)})
+        self.segments = [(t, off, min(self.SEG, n - off))
+                         for t, n in enumerate(w.numels) for off in range(0, n, self.SEG)]
+        self.step_no = 0
+
+    def _grads(self, step, t, start, n, scale):
+        w = self.w
+        g = [inputs.gen_host_u16(n, w.grad_recipe(step, i, t, scale), w.dtype, start, threads=1)
+             for i in range(w.k)]
+        inj = w.injection(step)
+        if inj is not None and inj[0] == t and start <= inj[1] < start + n:
+            g[-1][inj[1] - start] = INF16[w.dtype]
+        return g
+
+    def _acc(self, g, weights, n):
+        if self.w.k == 1:
+            return None
+        acc = np.empty(n, np.float32)
+        for i in range(self.w.k - 1):
+            oracle.accumulate_tensor(g[i], acc, self.dt, weights[i], i == 0)
+        return acc
+
+    def step(self):
+        from concurrent.futures import ThreadPoolExecutor
+        self.step_no += 1
+        w, s = self.w, self.step_no
+        weights = oracle.token_weights(w.token_counts(s))
+        S = self.scaler.scale
+        inv = oracle.unscale_factor(S)
+        mode = 1 if w.k == 1 else 2
+        done = [0]
+
+        def seg_sumsq(seg):
+            t, off, n = seg
+            g = self._grads(s, t, off, n, S)
+            acc = self._acc(g, weights, n)
+            r = oracle.unscale_sumsq_tensor(acc, g[-1], n, self.dt, weights[-1], mode, inv)
+            done[0] += 1
+            if done[0] % 64 == 0:
+                self.log("    oracle norm: %d/%d segments" % (done[0], len(self.segments)))
+            return r
+
+        with ThreadPoolExecutor(self.threads) as ex:
+            parts = list(ex.map(seg_sumsq, self.segments))
+        self.found_inf = any(p[0] for p in parts)
+        self.sumsq = oracle.sum_in_order([p[1] for p in parts])
+        self.norm, self.coef = oracle.norm_and_coef(self.sumsq, self.found_inf, w.max_norm)
+        if not self.found_inf:
+            b1, b2 = np.float32(w.hp["beta1"]), np.float32(w.hp["beta2"])
+            bc1, bc2 = oracle.bias_corrections(self.clock, b1, b2)
+            scale = oracle.update_scale(S, self.coef)
+            lam = oracle.decay(w.hp["weight_decay"], 1.0)
+            for (t, start, n), st in zip(self.windows, self.state):
+                st["prev_master"], st["prev_m"] = st["master"].copy(), st["m"].copy()
+                g = self._grads(s, t, start, n, S)
+                acc = self._acc(g, weights, n)
+                oracle.adamw_tensor(acc, g[-1], self.dt, weights[-1], mode, scale, st["master"],
+                                    st["m"], st["v"], st["w16"], w.hp["lr"], b1, b2, w.hp["eps"],
+                                    lam, bc1, bc2)
+            oracle.clock_advance(self.clock, b1, b2)
+        oracle.scaler_update(self.scaler, self.found_inf)
+
+
+def sample_windows(w, per_tensor=512, random_count=64, random_len=4099):
+    """First and last `per_tensor` elements of every tensor, plus seeded random windows."""
+    wins = []
+    for t, n in enumerate(w.numels):
+        wins.append((t, 0, min(per_tensor, n)))
+        if n > per_tensor:
+            lo = max(per_tensor, n - per_tensor)
+            wins.append((t, lo, n - lo))
+    k = inputs.key(w.cid, inputs.P_SAMPLE)
+    big = [t for t, n in enumerate(w.numels) if n > 2 * random_len]
+    for i in range(random_count):
+        t = big[inputs.draw(k, 2 * i) % len(big)]
+        start = inputs.draw(k, 2 * i + 1) % (w.numels[t] - random_len)
+        wins.append((t, start, random_len))
+    return wins
+
+
+def compare_windows(dev, so, w):
+    """Device state on the sampled windows against the streamed oracle; returns a report."""
+    torch = dev.torch
+    st = dev.stats()
+    rep = {"step": so.step_no, "found_inf": st["found_inf"], "scale": st["scale"],
+           "norm_gpu": st["grad_norm"], "norm_oracle": so.norm}
+    assert st["found_inf"] == int(so.found_inf), rep
+    assert st["scale"] == so.scaler.scale and st["good_steps"] == so.scaler.good_steps, rep
+    assert st["skipped"] == so.scaler.skipped, rep
+    assert st["step"] == so.clock.t, rep
+    assert st["beta1_pow"] == so.clock.p1 and st["beta2_pow"] == so.clock.p2, rep
+    if not so.found_inf:
+        assert abs(st["sumsq"] - so.sumsq) <= 1e-10 * so.sumsq, rep
+        assert abs(st["grad_norm"] - so.norm) <= 1e-5 * so.norm, rep
+    same = bool(so.found_inf) or (np.float32(st["grad_norm"]) == np.float32(so.norm)
+                                  and np.float32(st["clip_coef"]) == np.float32(so.coef))
+    rep["same_norm_bits"] = same
+    mism = 0
+    for (t, start, n), ost in zip(so.windows, so.state):
+        sl = slice(start, start + n)
+        got = {"master": dev.model.master[t][sl].cpu().numpy(),
+               "m": dev.model.m[t][sl].cpu().numpy(), "v": dev.model.v[t][sl].cpu().numpy(),
+               "w16": dev.model.w16[t][sl].cpu().view(torch.int16).numpy().view(np.uint16)}
+        assert np.array_equal(got["w16"], oracle.rd16(got["master"], so.dt)), "w16 != rd16(master)"
+        for name in ("master", "m", "v", "w16"):
+            a, b = got[name], ost[name]
+            if same:
+                if not np.array_equal(a, b):
+                    idx = int(np.flatnonzero(a != b)[0])
+                    raise AssertionError("%s differs: tensor %d element %d gpu %r oracle %r"
+                                         % (name, t, start + idx, a[idx], b[idx]))
+            elif name == "w16":
+                mism += int((a != b).sum())
+            else:
+                # 2e-6 relative to the magnitude of the terms each value is made of
+                b64 = b.astype(np.float64)
+                if name == "v":
+                    bound = 2e-6 * np.abs(b64)
+                elif name == "m":
+                    b1 = np.float64(np.float32(w.hp["beta1"]))
+                    m0 = ost["prev_m"].astype(np.float64)
+                    bound = 2e-6 * (b1 * np.abs(m0) + np.abs(b64 - b1 * m0))
+                else:
+                    w0 = ost["prev_master"].astype(np.float64)
+                    lam = w.hp["lr"] * w.hp["weight_decay"]
+                    bound = 2e-6 * (np.abs(w0) * (1 + lam) + np.abs(w0 - b64))
+                assert (np.abs(a.astype(np.float64) - b64) <= bound + 1e-45).all(), name
+    rep["w16_mismatch"] = mism
+    rep["windows"] = len(so.windows)
+    return rep

@@ -1,0 +1,44 @@
+"""Parity at the full sizes the benchmark times (needs an MI355X with ~210 GB free).
+
+The device runs the whole tensor list in the launch configuration bench.py uses;
+the oracle recomputes the global norm from regenerated inputs every step
+(streamed, all elements) and the update on sampled windows: the first and last
+512 elements of every tensor plus 64 seeded random windows of 4099 elements.
+"""
+import sys
+
+import pytest
+
+from inputs import configs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.timeout(1100)
+@pytest.mark.parametrize("name,steps", [("ragged-4096", 2), ("gpt-1.3B", 2), ("llama3-8B", 2)])
+def test_full_size_sampled_parity(name, steps):
+    import torch
+    from harness import DeviceRun, StreamedOracle, sample_windows, compare_windows
+    assert torch.cuda.is_available()
+    w = configs.make(name)
+    say("full-size %s: %d tensors, %d params, k=%d" % (name, len(w.tensors), w.total, w.k))
+    dev = DeviceRun(w)
+    so = StreamedOracle(w, sample_windows(w), log=say)
+    try:
+        for s in range(1, steps + 1):
+            scale = so.scaler.scale
+            dev.step(scale)
+            torch.cuda.synchronize()
+            say("  device step %d done" % s)
+            so.step()
+            rep = compare_windows(dev, so, w)
+            say("  step", s, rep)
+    finally:
+        dev.close()
+        del dev
+        torch.cuda.empty_cache()

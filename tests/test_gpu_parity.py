@@ -171,3 +171,31 @@ def test_call_order_and_argument_errors(mp):
         assert e.value.status == mp.MP_ERR_INVALID
     finally:
         dev.close()
+
+
+def test_scaler_grows_back_after_2000_clean_steps(mp):
+    """The fp16 run's controller: +inf on step 3 halves S (2^16 -> 2^15) and restarts the count;
+    2000 clean steps later (step 2003) S is 2^16 again.  Device and oracle agree on every
+    step's overflow flag, skip, S and count, and on the final state bit for bit."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make("gpt-124M-scaler")
+    orc = OracleRun(w, threads=1)
+    dev = DeviceRun(w)
+    trace = {}
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            st = dev.stats()
+            assert st["found_inf"] == int(orc.st.found_inf), s
+            assert st["scale"] == orc.st.scaler.scale and st["skipped"] == orc.st.scaler.skipped, s
+            assert st["good_steps"] == orc.st.scaler.good_steps, s
+            trace[s] = st["scale"]
+            if s % 500 == 0:
+                say("  step", s, "S", st["scale"], "count", st["good_steps"])
+        assert trace[2] == 2.0 ** 16 and trace[3] == 2.0 ** 15
+        assert trace[2002] == 2.0 ** 15 and trace[2003] == 2.0 ** 16
+        say(compare_step(dev, orc, w, w.steps))
+    finally:
+        dev.close()
