@@ -177,6 +177,22 @@ mp_status mp_gradset_destroy(mp_gradset* set);
 mp_status mp_state_create(const mp_scaler_cfg* cfg, mp_state** out);
 mp_status mp_state_destroy(mp_state* state);
 
+/* Save and restore the device state: loss scale, clean-step count, scaler
+ * configuration, optimizer step t and the beta powers ("Mixed precision ...",
+ * section 4 "The interface": state_dict / load_state_dict; section 5, pitfall
+ * 16: a resume that loses the count grows S late).  The fp32 masters, moments
+ * and 16-bit weights are the caller's buffers and are saved by the caller.
+ * A blob is MP_STATE_BLOB_BYTES bytes of host memory.
+ *  - export: writes the header at once and enqueues the copy of the device
+ *    state; the blob is complete once `stream` has reached this point.
+ *  - import: checks the header and every field on the host (MP_ERR_INVALID
+ *    for a foreign blob, another version, or out-of-range fields, leaving the
+ *    state untouched), then copies it to the device and waits for `stream`.
+ *    Call it between steps. */
+#define MP_STATE_BLOB_BYTES 256
+mp_status mp_state_export(const mp_state* state, void* blob, size_t blob_bytes, mp_stream stream);
+mp_status mp_state_import(mp_state* state, const void* blob, size_t blob_bytes, mp_stream stream);
+
 /* Enqueue a copy of the state into *out (host memory; pinned memory keeps the
  * call asynchronous).  *out is valid once `stream` has reached this point. */
 mp_status mp_state_read(const mp_state* state, mp_stats* out, mp_stream stream);
@@ -210,6 +226,26 @@ mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int3
 mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
                                 float w_last, int32_t last_is_first, float max_norm,
                                 mp_stream stream);
+
+/* The two halves of mp_unscale_check_norm, for a model whose parameters are
+ * sharded over ranks (ZeRO-1/2: each rank's plan covers its slice).  The norm
+ * must cover every shard ("Megatron Internals III", section 9: local squared
+ * norms reduced over the owning ranks; "Your weights fit on one device...",
+ * "Operational sharp edges: Gradient clipping"), and every rank must take the
+ * same skip decision (section 6).  One all-reduce of one binary64 value does
+ * both: an inf/NaN anywhere makes the sum non-finite.
+ *  - mp_norm_partial: writes this plan's fixed-order binary64 sum of squares
+ *    of g = g_eff/S (same g_eff as mp_unscale_check_norm) to partial_out, one
+ *    double in device memory.
+ *  - mp_norm_finish: from *sumsq (device; the sum over ranks, reduced in a
+ *    fixed rank order by the caller) sets found_inf = !isfinite(sumsq),
+ *    grad_norm and clip_coef exactly as mp_unscale_check_norm does.  Must
+ *    follow mp_norm_partial on the same plan and state (else MP_ERR_ORDER);
+ *    mp_adamw_step may follow it as it follows mp_unscale_check_norm. */
+mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                          int32_t last_is_first, double* partial_out, mp_stream stream);
+mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, float max_norm,
+                         mp_stream stream);
 
 /* AdamW + RNE cast ("Your weights fit on one device...", the Adam update;
  * "Accumulate gradients...", decoupled decay; "Mixed precision ...", section 2

@@ -29,7 +29,10 @@ ENTRY_POINTS = [
     "mp_gradset_create", "mp_gradset_destroy", "mp_state_create", "mp_state_destroy",
     "mp_state_read", "mp_state_scale_ptr", "mp_accumulate", "mp_unscale_check_norm",
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
+    "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
 ]
+
+MP_STATE_BLOB_BYTES = 256
 
 
 class MpError(RuntimeError):
@@ -103,6 +106,10 @@ def _bind(L):
         "mp_scaler_update": ([P, P], i32),
         "mp_cast_to_16": ([P, P, i64, i32, P], i32),
         "mp_widen_16": ([P, P, i64, i32, P], i32),
+        "mp_state_export": ([P, P, ctypes.c_size_t, P], i32),
+        "mp_state_import": ([P, P, ctypes.c_size_t, P], i32),
+        "mp_norm_partial": ([P, P, P, f32, i32, P, P], i32),
+        "mp_norm_finish": ([P, P, P, f32, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -260,6 +267,24 @@ def mp_widen_16(src, dst, n, dtype, stream=None):
                              _stream(stream)))
 
 
+def mp_state_export(state, blob_ptr, blob_bytes=MP_STATE_BLOB_BYTES, stream=None):
+    _check(lib().mp_state_export(state, ctypes.c_void_p(blob_ptr), blob_bytes, _stream(stream)))
+
+
+def mp_state_import(state, blob_ptr, blob_bytes=MP_STATE_BLOB_BYTES, stream=None):
+    _check(lib().mp_state_import(state, ctypes.c_void_p(blob_ptr), blob_bytes, _stream(stream)))
+
+
+def mp_norm_partial(plan, state, last, w_last, last_is_first, partial_out, stream=None):
+    _check(lib().mp_norm_partial(plan, state, last, float(w_last), int(bool(last_is_first)),
+                                 ctypes.c_void_p(partial_out), _stream(stream)))
+
+
+def mp_norm_finish(plan, state, sumsq, max_norm, stream=None):
+    _check(lib().mp_norm_finish(plan, state, ctypes.c_void_p(sumsq), float(max_norm),
+                                _stream(stream)))
+
+
 # --- convenience ---------------------------------------------------------------
 
 def scaler_cfg(init_scale=2.0 ** 16, growth=2.0, backoff=0.5, min_scale=1.0, max_scale=2.0 ** 64,
@@ -269,6 +294,20 @@ def scaler_cfg(init_scale=2.0 ** 16, growth=2.0, backoff=0.5, min_scale=1.0, max
 
 def adamw_hparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1):
     return AdamWHparams(lr, beta1, beta2, eps, weight_decay)
+
+
+def save_state(state, stream=None):
+    """The state blob as bytes (enqueues the copy, then waits for the stream)."""
+    buf = torch.empty(MP_STATE_BLOB_BYTES, dtype=torch.uint8, pin_memory=True)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    mp_state_export(state, buf.data_ptr(), MP_STATE_BLOB_BYTES, s)
+    s.synchronize()
+    return bytes(buf.numpy())
+
+
+def load_state(state, blob, stream=None):
+    buf = ctypes.create_string_buffer(bytes(blob), len(blob))
+    mp_state_import(state, ctypes.addressof(buf), len(blob), stream)
 
 
 def read_stats(state, stream=None):

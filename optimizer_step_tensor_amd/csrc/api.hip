@@ -27,7 +27,9 @@ struct mp_plan {
     TensorDesc* d_tensors;
     Chunk* d_chunks;
     double* d_partials;       // norm_grid entries
-    // call-order bookkeeping: mp_adamw_step must follow mp_unscale_check_norm
+    // call-order bookkeeping: mp_adamw_step must follow mp_unscale_check_norm (or
+    // mp_norm_partial + mp_norm_finish)
+    bool partial_pending;
     bool norm_pending;
     const mp_state* norm_state;
     const mp_gradset* norm_last;
@@ -420,6 +422,66 @@ mp_status mp_state_read(const mp_state* state, mp_stats* out, mp_stream stream)
     return ok();
 }
 
+namespace {
+
+const char kBlobMagic[8] = {'M', 'P', 'S', 'T', 'A', 'T', 'E', '1'};
+constexpr uint32_t kBlobHeader = 16;
+
+mp_status check_scaler_fields(const DevState& d)
+{
+    mp_scaler_cfg c{d.s.scale, d.growth, d.backoff, d.min_scale, d.max_scale, d.interval, d.enabled};
+    if (!is_pow2(c.init_scale) || !is_pow2(c.growth) || !is_pow2(c.backoff) ||
+        !is_pow2(c.min_scale) || !is_pow2(c.max_scale) || c.growth < 1.0f || c.backoff > 1.0f ||
+        !(c.min_scale <= c.init_scale && c.init_scale <= c.max_scale) || c.interval < 1)
+        return fail(MP_ERR_INVALID, "state blob: scaler fields out of range");
+    if (d.s.good_steps < 0 || d.s.good_steps >= d.interval || d.s.step < 0 || d.s.skipped_total < 0)
+        return fail(MP_ERR_INVALID, "state blob: counters out of range");
+    if (!(d.s.beta1_pow > 0.0 && d.s.beta1_pow <= 1.0 && d.s.beta2_pow > 0.0 && d.s.beta2_pow <= 1.0))
+        return fail(MP_ERR_INVALID, "state blob: beta powers out of range");
+    return MP_OK;
+}
+
+}  // namespace
+
+mp_status mp_state_export(const mp_state* state, void* blob, size_t blob_bytes, mp_stream stream)
+{
+    if (state == nullptr || blob == nullptr) return fail(MP_ERR_INVALID, "state and blob are required");
+    if (blob_bytes < MP_STATE_BLOB_BYTES) return fail(MP_ERR_INVALID, "blob needs MP_STATE_BLOB_BYTES bytes");
+    static_assert(kBlobHeader + sizeof(DevState) <= MP_STATE_BLOB_BYTES, "blob too small");
+    unsigned char* b = static_cast<unsigned char*>(blob);
+    std::memset(b, 0, MP_STATE_BLOB_BYTES);
+    std::memcpy(b, kBlobMagic, 8);
+    const uint32_t version = MPSTEP_ABI_VERSION, payload = sizeof(DevState);
+    std::memcpy(b + 8, &version, 4);
+    std::memcpy(b + 12, &payload, 4);
+    hipError_t e = hipMemcpyAsync(b + kBlobHeader, state->d, sizeof(DevState), hipMemcpyDeviceToHost,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    return ok();
+}
+
+mp_status mp_state_import(mp_state* state, const void* blob, size_t blob_bytes, mp_stream stream)
+{
+    if (state == nullptr || blob == nullptr) return fail(MP_ERR_INVALID, "state and blob are required");
+    if (blob_bytes < MP_STATE_BLOB_BYTES) return fail(MP_ERR_INVALID, "blob needs MP_STATE_BLOB_BYTES bytes");
+    const unsigned char* b = static_cast<const unsigned char*>(blob);
+    uint32_t version = 0, payload = 0;
+    std::memcpy(&version, b + 8, 4);
+    std::memcpy(&payload, b + 12, 4);
+    if (std::memcmp(b, kBlobMagic, 8) != 0 || version != MPSTEP_ABI_VERSION || payload != sizeof(DevState))
+        return fail(MP_ERR_INVALID, "not a state blob of this library version");
+    DevState d;
+    std::memcpy(&d, b + kBlobHeader, sizeof d);
+    mp_status st = check_scaler_fields(d);
+    if (st != MP_OK) return st;
+    d.inv_scale = 1.0f / d.s.scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(state->d, &d, sizeof d, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);   // `d` lives on this stack frame
+    if (e != hipSuccess) return hip_fail(e, "state import");
+    return ok();
+}
+
 mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale)
 {
     if (state == nullptr || dev_scale == nullptr) return fail(MP_ERR_INVALID, "state and out are required");
@@ -452,11 +514,52 @@ mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset
                                     grad_mode(last, last_is_first), plan->dtype, plan->d_partials,
                                     max_norm, state->d, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm launch");
+    plan->partial_pending = false;
     plan->norm_pending = true;
     plan->norm_state = state;
     plan->norm_last = last;
     plan->norm_w_last = w_last;
     plan->norm_last_is_first = last_is_first ? 1 : 0;
+    return ok();
+}
+
+mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                          int32_t last_is_first, double* partial_out, mp_stream stream)
+{
+    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
+    if (partial_out == nullptr || (reinterpret_cast<uintptr_t>(partial_out) & 7u) != 0)
+        return fail(MP_ERR_INVALID, "partial_out must be an 8-byte aligned device pointer");
+    mp_status st = check_last(plan, last, w_last, last_is_first);
+    if (st != MP_OK) return st;
+    hipError_t e = mpk::launch_norm_partial(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr,
+                                            w_last, grad_mode(last, last_is_first), plan->dtype,
+                                            plan->d_partials, state->d, partial_out,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "norm partial launch");
+    plan->partial_pending = true;
+    plan->norm_pending = false;
+    plan->norm_state = state;
+    plan->norm_last = last;
+    plan->norm_w_last = w_last;
+    plan->norm_last_is_first = last_is_first ? 1 : 0;
+    return ok();
+}
+
+mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, float max_norm,
+                         mp_stream stream)
+{
+    if (plan == nullptr || state == nullptr || sumsq == nullptr)
+        return fail(MP_ERR_INVALID, "plan, state and sumsq are required");
+    if ((reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0)
+        return fail(MP_ERR_INVALID, "sumsq must be 8-byte aligned");
+    if (std::isnan(max_norm) || std::isinf(max_norm)) return fail(MP_ERR_INVALID, "max_norm must be finite");
+    if (!plan->partial_pending || plan->norm_state != state)
+        return fail(MP_ERR_ORDER, "mp_norm_finish must follow mp_norm_partial on the same plan "
+                                  "and state");
+    hipError_t e = mpk::launch_norm_apply(sumsq, max_norm, state->d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "norm finish launch");
+    plan->partial_pending = false;
+    plan->norm_pending = true;
     return ok();
 }
 

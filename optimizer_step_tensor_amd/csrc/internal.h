@@ -90,6 +90,10 @@ hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const*
 hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
                        int mode, int dtype, double* partials, float max_norm, DevState* st,
                        hipStream_t s);
+hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* const* last,
+                               float w_last, int mode, int dtype, double* partials,
+                               const DevState* st, double* out, hipStream_t s);
+hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s);
 hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
                         int mode, int dtype, const AdamArgs& a, DevState* st, hipStream_t s);
 hipError_t launch_scaler(DevState* st, hipStream_t s);

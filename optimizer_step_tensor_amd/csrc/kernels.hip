@@ -317,6 +317,37 @@ __global__ __launch_bounds__(kBlock) void k_norm_finish(const double* __restrict
     }
 }
 
+// The two halves of k_norm_finish, for a norm whose sum of squares is reduced
+// across ranks between them: this plan's fixed-order total, then the finish
+// from a (summed) total.
+__global__ __launch_bounds__(kBlock) void k_norm_reduce(const double* __restrict__ partials, int n,
+                                                        double* __restrict__ out)
+{
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += kBlock) s += partials[i];
+    const double total = block_sum(s);
+    if (threadIdx.x == 0) out[0] = total;
+}
+
+__global__ void k_norm_apply(const double* __restrict__ sumsq, float max_norm,
+                             DevState* __restrict__ st)
+{
+    if (threadIdx.x != 0) return;
+    const double total = sumsq[0];
+    const int found_inf = !__builtin_isfinite(total);
+    const float norm = static_cast<float>(__builtin_sqrt(total));
+    float coef = 1.0f;
+    if (max_norm > 0.0f && !found_inf) {
+        const float q = max_norm / (norm + 1e-6f);
+        coef = q < 1.0f ? q : 1.0f;
+    }
+    st->s.found_inf = found_inf;
+    st->s.sumsq = total;
+    st->s.grad_norm = norm;
+    st->s.clip_coef = coef;
+    st->update_scale = st->inv_scale * coef;
+}
+
 // ---------------------------------------------------------------------------
 // AdamW on fp32 master/m/v and the RNE cast to the 16-bit weight.
 // ---------------------------------------------------------------------------
@@ -495,6 +526,32 @@ hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     k_norm_finish<<<1, kBlock, 0, s>>>(partials, grid, max_norm, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* const* last,
+                               float w_last, int mode, int dtype, double* partials,
+                               const DevState* st, double* out, hipStream_t s)
+{
+    DevState* stm = const_cast<DevState*>(st);
+    if (dtype == MP_BF16) {
+        if (mode == kAccOnly)       launch_norm_t<MP_BF16, kAccOnly>(p, grid, last, w_last, partials, stm, s);
+        else if (mode == kLastOnly) launch_norm_t<MP_BF16, kLastOnly>(p, grid, last, w_last, partials, stm, s);
+        else                        launch_norm_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, partials, stm, s);
+    } else {
+        if (mode == kAccOnly)       launch_norm_t<MP_FP16, kAccOnly>(p, grid, last, w_last, partials, stm, s);
+        else if (mode == kLastOnly) launch_norm_t<MP_FP16, kLastOnly>(p, grid, last, w_last, partials, stm, s);
+        else                        launch_norm_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, partials, stm, s);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k_norm_reduce<<<1, kBlock, 0, s>>>(partials, grid, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s)
+{
+    k_norm_apply<<<1, 64, 0, s>>>(sumsq, max_norm, st);
     return hipGetLastError();
 }
 

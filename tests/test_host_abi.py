@@ -132,3 +132,12 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_cast_to_16(ctypes.c_void_p(0x10004), ctypes.c_void_p(0x10000), 4, 0,
                            None) == mp.MP_ERR_ALIGN
     assert L.mp_cast_to_16(None, None, 0, 0, None) == mp.MP_OK      # empty cast: nothing to do
+    # a foreign or truncated state blob is refused before the state is touched
+    fake_state = ctypes.c_void_p(0x10000)
+    blob = ctypes.create_string_buffer(mp.MP_STATE_BLOB_BYTES)
+    assert L.mp_state_import(fake_state, blob, mp.MP_STATE_BLOB_BYTES, None) == mp.MP_ERR_INVALID
+    assert L.mp_state_import(fake_state, blob, 16, None) == mp.MP_ERR_INVALID
+    assert L.mp_state_export(fake_state, blob, 16, None) == mp.MP_ERR_INVALID
+    assert L.mp_norm_finish(None, None, None, 1.0, None) == mp.MP_ERR_INVALID
+    assert (L.mp_norm_partial(fake_state, fake_state, None, 1.0, 0, ctypes.c_void_p(0x10001), None)
+            == mp.MP_ERR_INVALID)
