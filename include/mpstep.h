@@ -279,6 +279,20 @@ mp_status mp_cast_to_16(const float* src, uint16_t* dst, int64_t n, mp_dtype16 d
 mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dtype,
                       mp_stream stream);
 
+/* Fine-grained FP8 cast ("Chapter 41 Training at Scale", section 41.5,
+ * listing 41.5), e.g. of the updated fp32 masters for an FP8 forward pass.
+ * For each block of `block` consecutive values (block a multiple of 16 in
+ * [16, 1024]; n a multiple of block, else MP_ERR_INVALID):
+ *   scales[b] = fl(max|x| / 448), or 1 for an all-zero block (NaNs are
+ *   ignored by the maximum);
+ *   codes[i]  = E4M3(fl(x_i / scales[b])): 1 sign, 4 exponent bits (bias 7),
+ *   3 mantissa bits, round to nearest even, saturating at 448 (E4M3 has no
+ *   infinity), NaN -> S.1111.111.
+ * Dequantisation is value(codes[i]) * scales[b].  src and codes 16-byte
+ * aligned, scales 4-byte aligned; n/block scales are written. */
+mp_status mp_cast_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n,
+                             int32_t block, mp_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

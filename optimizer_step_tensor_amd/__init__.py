@@ -30,6 +30,7 @@ ENTRY_POINTS = [
     "mp_state_read", "mp_state_scale_ptr", "mp_accumulate", "mp_unscale_check_norm",
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
+    "mp_cast_fp8_blocks",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -110,6 +111,7 @@ def _bind(L):
         "mp_state_import": ([P, P, ctypes.c_size_t, P], i32),
         "mp_norm_partial": ([P, P, P, f32, i32, P, P], i32),
         "mp_norm_finish": ([P, P, P, f32, P], i32),
+        "mp_cast_fp8_blocks": ([P, P, P, i64, i32, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -283,6 +285,11 @@ def mp_norm_partial(plan, state, last, w_last, last_is_first, partial_out, strea
 def mp_norm_finish(plan, state, sumsq, max_norm, stream=None):
     _check(lib().mp_norm_finish(plan, state, ctypes.c_void_p(sumsq), float(max_norm),
                                 _stream(stream)))
+
+
+def mp_cast_fp8_blocks(src, codes, scales, n, block=16, stream=None):
+    _check(lib().mp_cast_fp8_blocks(ctypes.c_void_p(src), ctypes.c_void_p(codes),
+                                    ctypes.c_void_p(scales), int(n), int(block), _stream(stream)))
 
 
 # --- convenience ---------------------------------------------------------------

@@ -615,4 +615,20 @@ mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dty
     return ok();
 }
 
+mp_status mp_cast_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n,
+                             int32_t block, mp_stream stream)
+{
+    if (block < 16 || block > 1024 || block % 16 != 0)
+        return fail(MP_ERR_INVALID, "block must be a multiple of 16 in [16, 1024]");
+    if (n < 0 || n % block != 0) return fail(MP_ERR_INVALID, "n must be a multiple of block");
+    if (n > 0 && (src == nullptr || codes == nullptr || scales == nullptr))
+        return fail(MP_ERR_INVALID, "NULL buffer");
+    if (!aligned16(src) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+        return fail(MP_ERR_ALIGN, "src and codes must be 16-byte aligned, scales 4-byte aligned");
+    hipError_t e = mpk::launch_fp8_blocks(src, codes, scales, n, block,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fp8 launch");
+    return ok();
+}
+
 }  // extern "C"

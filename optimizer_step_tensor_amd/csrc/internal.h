@@ -98,6 +98,8 @@ hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last
                         int mode, int dtype, const AdamArgs& a, DevState* st, hipStream_t s);
 hipError_t launch_scaler(DevState* st, hipStream_t s);
 hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s);
+hipError_t launch_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n, int block,
+                             hipStream_t s);
 hipError_t launch_widen_16(const uint16_t* src, float* dst, int64_t n, int dtype, hipStream_t s);
 
 }  // namespace mpk

@@ -474,6 +474,94 @@ __global__ __launch_bounds__(kBlock) void k_widen_16(const uint16_t* __restrict_
         dst[i] = widen16<DT>(src[i]);
 }
 
+// ---------------------------------------------------------------------------
+// Fine-grained FP8 ("Chapter 41 Training at Scale", section 41.5): one lane
+// per block of values; scale = max|x| / 448 (a zero block takes 1); each
+// value x / scale rounded to E4M3 (4 exponent bits, bias 7, 3 mantissa bits,
+// no infinity: saturate at 448; NaN -> S.1111.111).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7Fu;                  // NaN
+    if (a >= 0x43E80000u) return sign | 0x7Eu;                 // >= 464 (incl. inf): 448
+    if (a >= 0x3C800000u) {                                    // >= 2^-6: normal
+        // round the 23-bit mantissa to 3 bits, ties to even, then rebias 127 -> 7
+        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        return sign | ((r >> 20) - (120u << 3));
+    }
+    // subnormal: the nearest multiple of 2^-9 (ties to even); 8 * 2^-9 is the
+    // smallest normal, whose code is 8 as well
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | static_cast<uint32_t>(m);
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
+{
+    return e4m3_code(x.v[0] / scale) | (e4m3_code(x.v[1] / scale) << 8) |
+           (e4m3_code(x.v[2] / scale) << 16) | (e4m3_code(x.v[3] / scale) << 24);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool SIXTEEN>
+__global__ __launch_bounds__(kBlock) void k_fp8_blocks(const float* __restrict__ src,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales,
+                                                       int64_t nblocks, int block)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t b = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; b < nblocks;
+         b += stride) {
+        const float* x = src + b * block;
+        uint8_t* out = codes + b * block;
+        float amax = 0.0f;
+        if (SIXTEEN) {
+            // one pass: the 16 values stay in registers
+            F4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[q] = load_f4<true>(x + 4 * q, kGroup);
+#pragma unroll
+                for (int k = 0; k < kGroup; ++k) {
+                    const float a = __builtin_fabsf(v[q].v[k]);
+                    amax = a > amax ? a : amax;                // a NaN never wins
+                }
+            }
+            float scale = amax / 448.0f;
+            if (scale == 0.0f) scale = 1.0f;
+            u32x4 w;
+            w.x = pack_e4m3(v[0], scale); w.y = pack_e4m3(v[1], scale);
+            w.z = pack_e4m3(v[2], scale); w.w = pack_e4m3(v[3], scale);
+            *(MPK_GLOBAL u32x4*)(out) = w;
+            scales[b] = scale;
+        } else {
+            // two passes; the second re-reads the block from cache
+            for (int i = 0; i < block; i += kGroup) {
+                const F4 v = load_f4<true>(x + i, kGroup);
+#pragma unroll
+                for (int k = 0; k < kGroup; ++k) {
+                    const float a = __builtin_fabsf(v.v[k]);
+                    amax = a > amax ? a : amax;
+                }
+            }
+            float scale = amax / 448.0f;
+            if (scale == 0.0f) scale = 1.0f;
+            for (int i = 0; i < block; i += 16) {
+                u32x4 w;
+                w.x = pack_e4m3(load_f4<true>(x + i, kGroup), scale);
+                w.y = pack_e4m3(load_f4<true>(x + i + 4, kGroup), scale);
+                w.z = pack_e4m3(load_f4<true>(x + i + 8, kGroup), scale);
+                w.w = pack_e4m3(load_f4<true>(x + i + 12, kGroup), scale);
+                *(MPK_GLOBAL u32x4*)(out + i) = w;
+            }
+            scales[b] = scale;
+        }
+    }
+}
+
 unsigned elementwise_grid(int64_t n)
 {
     int64_t blocks = (n + kBlock - 1) / kBlock;
@@ -584,6 +672,16 @@ hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dty
     if (n == 0) return hipSuccess;
     if (dtype == MP_BF16) k_cast_to_16<MP_BF16><<<elementwise_grid(n), kBlock, 0, s>>>(src, dst, n);
     else                  k_cast_to_16<MP_FP16><<<elementwise_grid(n), kBlock, 0, s>>>(src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n, int block,
+                             hipStream_t s)
+{
+    const int64_t nblocks = n / block;
+    if (nblocks == 0) return hipSuccess;
+    if (block == 16) k_fp8_blocks<true><<<elementwise_grid(nblocks), kBlock, 0, s>>>(src, codes, scales, nblocks, block);
+    else             k_fp8_blocks<false><<<elementwise_grid(nblocks), kBlock, 0, s>>>(src, codes, scales, nblocks, block);
     return hipGetLastError();
 }
 

@@ -85,6 +85,13 @@ def _bind(L):
     L.or_update_scale.restype = f32
     L.or_decay.argtypes = [f32, f32]
     L.or_decay.restype = f32
+    L.or_e4m3.argtypes = [f32]
+    L.or_e4m3.restype = ctypes.c_uint8
+    L.or_e4m3_array.argtypes = [_P, _P, i64]
+    L.or_e4m3_value.argtypes = [ctypes.c_uint8]
+    L.or_e4m3_value.restype = f32
+    L.or_fp8_block_cast.argtypes = [_P, i64, i32, _P, _P]
+    L.or_fp8_block_cast.restype = i32
     L.or_model_state_bytes.argtypes = [i64]
     L.or_model_state_bytes.restype = i64
     return L
@@ -225,6 +232,33 @@ def model_state_bytes(params, L=None):
     """2 + 2 + 4 + 4 + 4 bytes per parameter ([TS] equation (41.1))."""
     L = L or lib()
     return L.or_model_state_bytes(int(params))
+
+
+def e4m3(x, L=None):
+    """E4M3 codes of fp32 values (RNE, saturating at 448) ([TS] section 41.5)."""
+    L = L or lib()
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(x.size, np.uint8)
+    L.or_e4m3_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def e4m3_value(codes, L=None):
+    L = L or lib()
+    return np.array([L.or_e4m3_value(int(c)) for c in np.asarray(codes).ravel()], np.float32)
+
+
+def fp8_block_cast(x, block=16, L=None):
+    """(codes, scales) of the fine-grained FP8 cast ([TS] section 41.5, listing 41.5)."""
+    L = L or lib()
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    if block <= 0 or x.size % block:
+        raise ValueError("the length must be divisible by block")
+    codes = np.empty(x.size, np.uint8)
+    scales = np.empty(x.size // block, np.float32)
+    if L.or_fp8_block_cast(_ptr(x), x.size, block, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("the length must be divisible by block")
+    return codes, scales
 
 
 def make_scaler(init_scale=2.0 ** 16, growth=2.0, backoff=0.5, min_scale=1.0,

@@ -29,7 +29,8 @@
  *        (token-weighted accumulation equations), "Extend the existing update
  *        and reverse owners" (count validation), "Discard a failed partial
  *        logical update" (what a skipped update preserves).
- *  [TS]  "Chapter 41 Training at Scale": section 41.1, equation (41.1).
+ *  [TS]  "Chapter 41 Training at Scale": section 41.1, equation (41.1);
+ *        section 41.5, fine-grained FP8 scaling (listing 41.5).
  *
  * Readings where the pages are silent (each one is listed in the design notes):
  *  - AdamW: the pages describe it only in words ([ZQ]); the per-element
@@ -43,6 +44,9 @@
  *    on committed steps ([RS]: a skipped attempt keeps the "beta powers").
  *  - NaN inputs to the 16-bit rounding give the format's quiet NaN with the
  *    sign kept; the payload is not specified by the pages.
+ *  - FP8: the chapter's E4M3 emulator is not printed; or_e4m3 rounds to
+ *    nearest, ties to even, saturates at the largest finite value 448 (E4M3
+ *    has no infinity), and maps NaN to S.1111.111.
  */
 #include <math.h>
 #include <stdint.h>
@@ -431,4 +435,74 @@ void or_scaler_update(or_scaler* s, int found_inf)
 int64_t or_model_state_bytes(int64_t params)
 {
     return params * (2 + 2 + 4 + 4 + 4);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fine-grained FP8 scaling ([TS] section 41.5, listing 41.5): per block of  */
+/* `block` values, scale = max|x| / 448 in fp32 (a zero block takes scale    */
+/* 1), then every value x / scale is rounded to E4M3.                          */
+/* E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinities; the  */
+/* largest finite value is 1.75 * 2^8 = 448 (S.1111.111 is NaN), the smallest */
+/* normal 2^-6, the smallest subnormal 2^-9.                                   */
+/* ------------------------------------------------------------------------ */
+uint8_t or_e4m3(float x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    if (isnan(x)) return (uint8_t)(sign | 0x7F);
+    double X = fabs((double)x);
+    if (X == 0.0) return sign;
+    double Y;
+    if (isinf(X)) {
+        Y = 448.0;
+    } else {
+        int E;
+        frexp(X, &E);
+        int e = E - 1;
+        if (e < -6) e = -6;                       /* subnormal quantum below 2^-6 */
+        double quantum = ldexp(1.0, e - 3);
+        Y = nearbyint(X / quantum) * quantum;     /* nearest, ties to even */
+        if (Y > 448.0) Y = 448.0;                 /* saturate */
+    }
+    if (Y == 0.0) return sign;
+    int E;
+    frexp(Y, &E);
+    int e = E - 1;
+    if (e >= -6) {
+        uint32_t mant = (uint32_t)((Y / ldexp(1.0, e) - 1.0) * 8.0);
+        return (uint8_t)(sign | (uint32_t)((e + 7) << 3) | mant);
+    }
+    return (uint8_t)(sign | (uint32_t)(Y / ldexp(1.0, -9)));
+}
+
+void or_e4m3_array(const float* x, uint8_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = or_e4m3(x[i]);
+}
+
+float or_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, E = (c >> 3) & 0xF, M = c & 7;
+    if (E == 0xF && M == 7) return NAN;
+    double v = E == 0 ? ldexp((double)M, -9) : ldexp(1.0 + M / 8.0, E - 7);
+    return (float)(s ? -v : v);
+}
+
+/* Returns 0, or -1 when n is not a multiple of block (the listing refuses a
+ * last dimension that the block size does not divide). */
+int or_fp8_block_cast(const float* x, int64_t n, int32_t block, uint8_t* codes, float* scales)
+{
+    if (block <= 0 || n % block != 0) return -1;
+    for (int64_t b = 0; b < n / block; ++b) {
+        const float* xb = x + b * block;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < block; ++i) {
+            float a = fabsf(xb[i]);
+            if (a > amax) amax = a;
+        }
+        float scale = amax / 448.0f;
+        if (scale == 0.0f) scale = 1.0f;
+        scales[b] = scale;
+        for (int32_t i = 0; i < block; ++i) codes[b * block + i] = or_e4m3(xb[i] / scale);
+    }
+    return 0;
 }

@@ -23,8 +23,8 @@ STEP = "step.py"
 
 # (id, file, original text, mutated text)
 MUTANTS = [
-    ("rd16-truncates", C, "nearbyint(X / quantum)", "trunc(X / quantum)"),
-    ("rd16-ties-away", C, "nearbyint(X / quantum)", "round(X / quantum)"),
+    ("rd16-truncates", C, "double r = nearbyint(X / quantum);", "double r = trunc(X / quantum);"),
+    ("rd16-ties-away", C, "double r = nearbyint(X / quantum);", "double r = round(X / quantum);"),
     ("rd16-no-overflow", C, "if (fabs(Y) > or_max_finite(f)) Y = negative ? -INFINITY : INFINITY;",
      ""),
     ("rd16-nan-not-quiet", C, "| emask | quiet);", "| emask);"),
@@ -96,6 +96,17 @@ MUTANTS = [
     ("skip-not-recorded", C, "s->skipped = found_inf ? 1 : 0;", "s->skipped = 0;"),
     ("accounting-drops-grad", C, "return params * (2 + 2 + 4 + 4 + 4);",
      "return params * (2 + 4 + 4 + 4);"),
+    ("fp8-scale-without-abs", C, "float a = fabsf(xb[i]);", "float a = xb[i];"),
+    ("fp8-zero-block-scale", C, "if (scale == 0.0f) scale = 1.0f;", ""),
+    ("fp8-multiplies-by-scale", C, "codes[b * block + i] = or_e4m3(xb[i] / scale);",
+     "codes[b * block + i] = or_e4m3(xb[i] * scale);"),
+    ("fp8-scale-wrong-max", C, "float scale = amax / 448.0f;", "float scale = amax / 480.0f;"),
+    ("e4m3-truncates", C, "Y = nearbyint(X / quantum) * quantum;", "Y = trunc(X / quantum) * quantum;"),
+    ("e4m3-bias", C, "return (uint8_t)(sign | (uint32_t)((e + 7) << 3) | mant);",
+     "return (uint8_t)(sign | (uint32_t)((e + 8) << 3) | mant);"),
+    ("e4m3-subnormal-quantum", C, "if (e < -6) e = -6;                       /* subnormal",
+     "if (e < -7) e = -7;                       /* subnormal"),
+    ("e4m3-no-saturation", C, "if (Y > 448.0) Y = 448.0;                 /* saturate */", ""),
     ("step-on-overflow (pitfall 12)", STEP, "        if self.found_inf:\n            return False\n",
      ""),
     ("clock-not-advanced", STEP, "        clock_advance(self.clock, beta1, beta2, self.L)\n", ""),

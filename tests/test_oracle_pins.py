@@ -624,3 +624,77 @@ def test_sixteen_bytes_per_parameter():
     assert oracle.model_state_bytes(1) == g["bytes_per_param"]["total"]
     ex = g["exercise_41_1"]
     assert oracle.model_state_bytes(ex["params"]) == ex["bytes"]
+
+
+# --- fine-grained FP8 ('Chapter 41 Training at Scale', section 41.5) -----------------
+
+def test_e4m3_format_facts():
+    """E4M3: largest finite 448 (the listing's max_value), smallest normal 2^-6, smallest
+    subnormal 2^-9; ties go to even; NaN keeps its sign; no infinity (saturate at 448)."""
+    vals = [448.0, 2.0 ** -6, 2.0 ** -9, 2.0 ** -10, 1.0, 1.0625, 1.1875, 3 * 2.0 ** -10,
+            -1.5, float("inf"), 1e9, -0.0]
+    assert [int(c) for c in oracle.e4m3(vals)] == [0x7E, 0x08, 0x01, 0x00, 0x38, 0x38, 0x3A,
+                                                   0x02, 0xBC, 0x7E, 0x7E, 0x80]
+    assert oracle.e4m3([float("nan")])[0] & 0x7F == 0x7F
+    assert oracle.e4m3_value([0x7E])[0] == 448.0 and np.isnan(oracle.e4m3_value([0x7F])[0])
+
+
+def test_e4m3_roundtrip_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_value(codes)
+    ok = ~np.isnan(vals)
+    assert ok.sum() == 254
+    back = oracle.e4m3(vals[ok])
+    same = back == codes[ok]
+    # the two zeros both encode; -0 keeps its sign
+    assert same.all()
+
+
+def test_e4m3_vs_torch_float8():
+    """Special case reducing to a library routine: torch's float32 -> float8_e4m3fn (RNE) on every
+    sign/exponent/top-mantissa prefix with rounding-relevant tails, below the overflow threshold
+    464 (where torch returns NaN and this reading saturates)."""
+    import torch
+    x = _structured_patterns()
+    keep = np.isnan(x) | (np.abs(x) < 464.0)
+    x = x[keep]
+    mine = oracle.e4m3(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = np.isnan(x)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert ((mine[nan] & 0x7F) == 0x7F).all()
+
+
+def test_fp8_block_cast_follows_the_listing():
+    """Listing 41.5: scale = max|x|/max_value per block of 16 (a zero block takes 1); the
+    dequantised value x' = e4m3(x/scale) * scale is within half an E4M3 spacing of x."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal(16 * 64) * np.exp(rng.uniform(-8, 8, 16 * 64))).astype(np.float32)
+    x[32:48] = 0.0
+    codes, scales = oracle.fp8_block_cast(x, 16)
+    blocks = x.reshape(-1, 16)
+    want = np.max(np.abs(blocks), axis=1) / np.float32(448.0)
+    want = np.where(want == 0, np.float32(1.0), want).astype(np.float32)
+    assert np.array_equal(scales, want)
+    deq = (oracle.e4m3_value(codes).reshape(-1, 16) * scales[:, None]).astype(np.float32)
+    y = np.abs(blocks / scales[:, None])
+    bound = np.where(y >= 2.0 ** -6, 2.0 ** -4 * y, 2.0 ** -10) * scales[:, None] * (1 + 1e-6)
+    assert (np.abs(deq - blocks) <= bound).all()
+    with pytest.raises(ValueError):
+        oracle.fp8_block_cast(np.zeros(17, np.float32), 16)
+
+
+def test_fp8_block_scales_help_the_small_block():
+    """Section 41.5: one scale for a whole tensor forces small blocks onto a coarse step; a scale
+    per block keeps their relative precision."""
+    big = np.full(16, 1000.0, np.float32)
+    small = np.linspace(1e-3, 2e-3, 16).astype(np.float32)
+    x = np.concatenate([big, small])
+    c_blk, s_blk = oracle.fp8_block_cast(x, 16)
+    c_one, s_one = oracle.fp8_block_cast(x, 32)
+    d_blk = oracle.e4m3_value(c_blk) * np.repeat(s_blk, 16)
+    d_one = oracle.e4m3_value(c_one) * np.repeat(s_one, 32)
+    rel_blk = np.abs(d_blk[16:] - small) / small
+    rel_one = np.abs(d_one[16:] - small) / small
+    assert rel_blk.max() <= 2.0 ** -4
+    assert rel_one.max() >= 0.5                       # flushed to (nearly) zero
