@@ -107,13 +107,94 @@ def measured_traffic(workload):
     return t.get("bytes_per_launch")
 
 
+def time_launches(torch, stream, fn, reps):
+    """Average ms of `reps` calls of fn, HIP events on the library's stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_extras(mp, torch, w, model, g16, hp, weights, stream):
+    """The rows after the hot path, on the same resident buffers:
+    - the fine-grained FP8 cast (block 16) of every fp32 master;
+    - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
+      multiples of 8 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
+    out = {}
+    P, k = w.total, w.k
+    big = max(w.numels)
+    codes = torch.empty(big, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(big // 16 + 1, dtype=torch.float32, device="cuda")
+    cast = [(x, n - n % 16) for x, n in zip(model.master, w.numels) if n >= 16]
+
+    def fp8_all():
+        for x, n in cast:
+            mp.mp_cast_fp8_blocks(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), n, 16, stream)
+
+    ms = time_launches(torch, stream, fp8_all, 3)
+    n_cast = sum(n for _, n in cast)
+    gbps = n_cast * (4 + 1 + 4 / 16) / ms / 1e6
+    out["fp8_block_cast"] = {"block": 16, "elements": n_cast, "ms": ms,
+                             "bytes_per_element": 5.25, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+    ranks, r = 8, 0
+    numel, ptrs = [], {"acc": [], "master": [], "m": [], "v": [], "w16": []}
+    gp = [[] for _ in range(k)]
+    for t, n in enumerate(w.numels):
+        per = ((n + ranks - 1) // ranks + 7) // 8 * 8     # ceil(n / ranks), rounded up to 8
+        lo, hi = min(n, r * per), min(n, (r + 1) * per)
+        if hi <= lo:
+            continue
+        numel.append(hi - lo)
+        for name, esz in (("acc", 4), ("master", 4), ("m", 4), ("v", 4), ("w16", 2)):
+            ptrs[name].append(getattr(model, name)[t].data_ptr() + esz * lo)
+        for i in range(k):
+            gp[i].append(g16[i][t].data_ptr() + 2 * lo)
+    plan = mp.mp_plan_create(numel, model.dtype, ptrs["acc"], ptrs["master"], ptrs["m"],
+                             ptrs["v"], ptrs["w16"])
+    sets = [mp.mp_gradset_create(plan, g) for g in gp]
+    st = mp.mp_state_create(mp.scaler_cfg(init_scale=1.0, enabled=False))
+    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+
+    def shard_step():
+        for i in range(k - 1):
+            mp.mp_accumulate(plan, sets[i], weights[i], i == 0, stream)
+        mp.mp_norm_partial(plan, st, sets[-1], weights[-1], k == 1, part.data_ptr(), stream)
+        # (the all-reduce of the one partial sum would run here)
+        mp.mp_norm_finish(plan, st, part.data_ptr(), w.max_norm, stream)
+        mp.mp_adamw_step(plan, st, sets[-1], weights[-1], k == 1, hp, stream)
+        mp.mp_scaler_update(st, stream)
+
+    ms = time_launches(torch, stream, shard_step, 3)
+    p_share = sum(numel)
+    out["zero8_rank_share"] = {"params": p_share, "ms_per_step": ms,
+                               "params_per_s": p_share / (ms * 1e-3),
+                               "GBps": bytes_per_param(k)["step"] * p_share / ms / 1e6}
+    for g in sets:
+        mp.mp_gradset_destroy(g)
+    mp.mp_state_destroy(st)
+    mp.mp_plan_destroy(plan)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3-8B")
+    ap.add_argument("--layout", default="flat", choices=("tensor", "flat"),
+                    help="one allocation per tensor, or one flat buffer per kind of array")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="time this many single steps after warm-up and print each")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the FP8 block cast and one ZeRO-8 rank's slice")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -133,7 +214,7 @@ def main():
     torch.cuda.set_device(0)
     dt16 = mp.MP_BF16 if w.dtype == inputs.BF16 else mp.MP_FP16
     t16 = torch.bfloat16 if w.dtype == inputs.BF16 else torch.float16
-    model = mp.ModelState(w.numels, dt16, with_acc=k > 1)
+    model = mp.ModelState(w.numels, dt16, with_acc=k > 1, layout=args.layout)
     for t, x in enumerate(model.master):
         inputs.fill_dev_f32(x, w.master_recipe(t))
     for x, y in zip(model.master, model.w16):
@@ -144,7 +225,7 @@ def main():
     S0 = cfg.init_scale
     g16 = []
     for i in range(k):
-        g16.append([torch.empty(n, dtype=t16, device="cuda") for n in w.numels])
+        g16.append(model.grad_buffers())
         for t, x in enumerate(g16[-1]):
             inputs.fill_dev_u16(x, w.grad_recipe(1, i, t, S0), w.dtype)
     sets = [model.gradset(g) for g in g16]
@@ -192,6 +273,15 @@ def main():
     for _ in range(args.warmup):
         one_step(False)
     torch.cuda.synchronize()
+    if args.trace_steps:
+        for i in range(args.trace_steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            one_step(False)
+            b.record(stream)
+            b.synchronize()
+            log("trace step %d: %.3f ms" % (i, a.elapsed_time(b)))
     t0 = time.perf_counter()
     g0 = torch.cuda.Event(enable_timing=True)
     g1 = torch.cuda.Event(enable_timing=True)
@@ -217,6 +307,7 @@ def main():
         % (ms_per_step, step_bytes / ms_per_step / 1e6, step_bytes / ms_per_step / 1e6 /
            HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
 
+    extras = None if args.no_extras else run_extras(mp, torch, w, model, g16, hp, weights, stream)
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,
@@ -232,6 +323,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
         "config": {"workload": w.name, "params": P, "tensors": len(w.tensors), "k": k,
+                   "layout": args.layout,
                    "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
                    "schedule": "k-1 accumulate passes, last micro-batch folded into norm and "
                                "AdamW passes",
@@ -247,6 +339,7 @@ def main():
                      "bytes_per_param": bpp["adamw"],
                      "traffic": traffic},
         "cpu_baseline": None,
+        "extras": extras,
     }
     for s in sets:
         mp.mp_gradset_destroy(s)

@@ -326,25 +326,52 @@ def read_stats(state, stream=None):
     return Stats.from_buffer_copy(bytes(buf.numpy())).as_dict()
 
 
+def _align8(n):
+    return (n + 7) // 8 * 8
+
+
 class ModelState:
     """Device buffers of one model (torch allocations) and the plan over them.
 
     For each tensor: fp32 master, m, v, the 16-bit weight, and (with_acc) the
-    fp32 accumulation buffer.  ``g16`` gradient buffers are the caller's.
+    fp32 accumulation buffer.  ``layout="tensor"`` allocates every buffer of
+    every tensor separately; ``layout="flat"`` allocates one contiguous buffer
+    per kind (Megatron-style flattened buffers) and hands the plan per-tensor
+    views into it, each starting on a multiple of 8 elements (16-byte aligned
+    for every element size).  ``g16`` gradient buffers are the caller's;
+    ``grad_buffers`` makes them in the same layout.
     """
 
-    def __init__(self, numels, dtype, with_acc=True, wd_mult=None, device="cuda"):
+    def __init__(self, numels, dtype, with_acc=True, wd_mult=None, device="cuda",
+                 layout="tensor"):
         self.numels = [int(n) for n in numels]
         self.dtype = dtype
-        t16 = torch.bfloat16 if dtype == MP_BF16 else torch.float16
-        self.master = [torch.zeros(n, dtype=torch.float32, device=device) for n in self.numels]
-        self.m = [torch.zeros(n, dtype=torch.float32, device=device) for n in self.numels]
-        self.v = [torch.zeros(n, dtype=torch.float32, device=device) for n in self.numels]
-        self.w16 = [torch.zeros(n, dtype=t16, device=device) for n in self.numels]
-        self.acc = ([torch.zeros(n, dtype=torch.float32, device=device) for n in self.numels]
-                    if with_acc else None)
+        self.layout = layout
+        self.device = device
+        self.t16 = torch.bfloat16 if dtype == MP_BF16 else torch.float16
+        self.master = self._alloc(torch.float32)
+        self.m = self._alloc(torch.float32, zero=True)
+        self.v = self._alloc(torch.float32, zero=True)
+        self.w16 = self._alloc(self.t16, zero=True)
+        self.acc = self._alloc(torch.float32, zero=True) if with_acc else None
         self.plan = mp_plan_create(self.numels, dtype, self.acc, self.master, self.m, self.v,
                                    self.w16, wd_mult)
+
+    def _alloc(self, dt, zero=False):
+        make = torch.zeros if zero else torch.empty
+        if self.layout == "tensor":
+            return [make(n, dtype=dt, device=self.device) for n in self.numels]
+        assert self.layout == "flat", self.layout
+        offs, total = [], 0
+        for n in self.numels:
+            offs.append(total)
+            total += _align8(n)
+        flat = make(total, dtype=dt, device=self.device)
+        return [flat[o:o + n] for o, n in zip(offs, self.numels)]
+
+    def grad_buffers(self):
+        """One micro-batch's 16-bit gradient buffers, in this model's layout."""
+        return self._alloc(self.t16)
 
     def gradset(self, g16):
         return mp_gradset_create(self.plan, g16)

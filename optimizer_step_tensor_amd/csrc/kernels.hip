@@ -506,7 +506,51 @@ __device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool SIXTEEN>
+// Block of 16 (the listing's default): a wave covers 1024 consecutive values,
+// lane l holding values 4l..4l+3 of each 256-value slab, so every load and
+// store instruction of the wave is contiguous; the four lanes that hold one
+// block combine their maxima with two butterfly shuffles.
+__global__ __launch_bounds__(kBlock) void k_fp8_blocks16(const float* __restrict__ src,
+                                                         uint8_t* __restrict__ codes,
+                                                         float* __restrict__ scales,
+                                                         int64_t n)
+{
+    constexpr int kSlab = kWave * kGroup;                  // 256 values
+    constexpr int kWaveValues = 4 * kSlab;                 // 1024 values per wave pass
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + threadIdx.x / kWave;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * (kBlock / kWave);
+    for (int64_t base = wave * kWaveValues; base < n; base += waves * kWaveValues) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t e = base + j * kSlab + lane * kGroup;   // n is a multiple of 16
+            const bool live = e < n;
+            F4 v;
+            if (live) v = load_f4<true>(src + e, kGroup);
+            else v.v[0] = v.v[1] = v.v[2] = v.v[3] = 0.0f;
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k) {
+                const float a = __builtin_fabsf(v.v[k]);
+                amax = a > amax ? a : amax;                        // a NaN never wins
+            }
+#pragma unroll
+            for (int off = 1; off < 4; off <<= 1) {
+                const float o = __shfl_xor(amax, off, kWave);
+                amax = o > amax ? o : amax;
+            }
+            float scale = amax / 448.0f;
+            if (scale == 0.0f) scale = 1.0f;
+            if (live) {
+                *(MPK_GLOBAL uint32_t*)(codes + e) = pack_e4m3(v, scale);
+                if ((lane & 3) == 0) scales[e / 16] = scale;
+            }
+        }
+    }
+}
+
+// Other block sizes (multiples of 16): one lane per block, two passes; the
+// second re-reads the block from cache.
 __global__ __launch_bounds__(kBlock) void k_fp8_blocks(const float* __restrict__ src,
                                                        uint8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
@@ -518,47 +562,25 @@ __global__ __launch_bounds__(kBlock) void k_fp8_blocks(const float* __restrict__
         const float* x = src + b * block;
         uint8_t* out = codes + b * block;
         float amax = 0.0f;
-        if (SIXTEEN) {
-            // one pass: the 16 values stay in registers
-            F4 v[4];
+        for (int i = 0; i < block; i += kGroup) {
+            const F4 v = load_f4<true>(x + i, kGroup);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                v[q] = load_f4<true>(x + 4 * q, kGroup);
-#pragma unroll
-                for (int k = 0; k < kGroup; ++k) {
-                    const float a = __builtin_fabsf(v[q].v[k]);
-                    amax = a > amax ? a : amax;                // a NaN never wins
-                }
+            for (int k = 0; k < kGroup; ++k) {
+                const float a = __builtin_fabsf(v.v[k]);
+                amax = a > amax ? a : amax;
             }
-            float scale = amax / 448.0f;
-            if (scale == 0.0f) scale = 1.0f;
-            u32x4 w;
-            w.x = pack_e4m3(v[0], scale); w.y = pack_e4m3(v[1], scale);
-            w.z = pack_e4m3(v[2], scale); w.w = pack_e4m3(v[3], scale);
-            *(MPK_GLOBAL u32x4*)(out) = w;
-            scales[b] = scale;
-        } else {
-            // two passes; the second re-reads the block from cache
-            for (int i = 0; i < block; i += kGroup) {
-                const F4 v = load_f4<true>(x + i, kGroup);
-#pragma unroll
-                for (int k = 0; k < kGroup; ++k) {
-                    const float a = __builtin_fabsf(v.v[k]);
-                    amax = a > amax ? a : amax;
-                }
-            }
-            float scale = amax / 448.0f;
-            if (scale == 0.0f) scale = 1.0f;
-            for (int i = 0; i < block; i += 16) {
-                u32x4 w;
-                w.x = pack_e4m3(load_f4<true>(x + i, kGroup), scale);
-                w.y = pack_e4m3(load_f4<true>(x + i + 4, kGroup), scale);
-                w.z = pack_e4m3(load_f4<true>(x + i + 8, kGroup), scale);
-                w.w = pack_e4m3(load_f4<true>(x + i + 12, kGroup), scale);
-                *(MPK_GLOBAL u32x4*)(out + i) = w;
-            }
-            scales[b] = scale;
         }
+        float scale = amax / 448.0f;
+        if (scale == 0.0f) scale = 1.0f;
+        for (int i = 0; i < block; i += 16) {
+            u32x4 w;
+            w.x = pack_e4m3(load_f4<true>(x + i, kGroup), scale);
+            w.y = pack_e4m3(load_f4<true>(x + i + 4, kGroup), scale);
+            w.z = pack_e4m3(load_f4<true>(x + i + 8, kGroup), scale);
+            w.w = pack_e4m3(load_f4<true>(x + i + 12, kGroup), scale);
+            *(MPK_GLOBAL u32x4*)(out + i) = w;
+        }
+        scales[b] = scale;
     }
 }
 
@@ -680,8 +702,14 @@ hipError_t launch_fp8_blocks(const float* src, uint8_t* codes, float* scales, in
 {
     const int64_t nblocks = n / block;
     if (nblocks == 0) return hipSuccess;
-    if (block == 16) k_fp8_blocks<true><<<elementwise_grid(nblocks), kBlock, 0, s>>>(src, codes, scales, nblocks, block);
-    else             k_fp8_blocks<false><<<elementwise_grid(nblocks), kBlock, 0, s>>>(src, codes, scales, nblocks, block);
+    if (block == 16) {
+        int64_t waves = (n + 1023) / 1024;
+        int64_t grid = (waves + kBlock / kWave - 1) / (kBlock / kWave);
+        if (grid > 16384) grid = 16384;
+        k_fp8_blocks16<<<static_cast<unsigned>(grid), kBlock, 0, s>>>(src, codes, scales, n);
+    } else {
+        k_fp8_blocks<<<elementwise_grid(nblocks), kBlock, 0, s>>>(src, codes, scales, nblocks, block);
+    }
     return hipGetLastError();
 }
 

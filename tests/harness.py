@@ -65,20 +65,18 @@ class OracleRun:
 class DeviceRun:
     """The workload in device buffers, stepped by libmpstep."""
 
-    def __init__(self, w, sep_grads=True):
+    def __init__(self, w, sep_grads=True, layout="tensor"):
         import torch
         import optimizer_step_tensor_amd as mp
         self.torch, self.mp, self.w = torch, mp, w
         dt = mp.MP_BF16 if w.dtype == inputs.BF16 else mp.MP_FP16
-        self.model = mp.ModelState(w.numels, dt, with_acc=w.k > 1)
+        self.model = mp.ModelState(w.numels, dt, with_acc=w.k > 1, layout=layout)
         for t, x in enumerate(self.model.master):
             inputs.fill_dev_f32(x, w.master_recipe(t))
         for x, y in zip(self.model.master, self.model.w16):
             mp.mp_cast_to_16(x.data_ptr(), y.data_ptr(), x.numel(), dt)
-        t16 = torch.bfloat16 if w.dtype == inputs.BF16 else torch.float16
         n_sets = w.k if sep_grads else 1
-        self.g16 = [[torch.empty(n, dtype=t16, device="cuda") for n in w.numels]
-                    for _ in range(n_sets)]
+        self.g16 = [self.model.grad_buffers() for _ in range(n_sets)]
         self.gsets = [self.model.gradset(g) for g in self.g16]
         cfg = (mp.scaler_cfg(**w.scaler) if w.scaler is not None
                else mp.scaler_cfg(init_scale=1.0, enabled=False))

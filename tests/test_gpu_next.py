@@ -137,3 +137,72 @@ def test_sharded_norm_matches_unsharded(mp, name):
         for st in states:
             mp.mp_state_destroy(st)
         dev.close()
+
+
+@pytest.mark.parametrize("name", ["llama3-8B-small", "edges-fp16"])
+def test_flattened_buffers(mp, name):
+    """'Megatron Internals III' section 8 (flattened fp32 main-gradient buffers): the model's
+    buffers as one contiguous allocation per kind with per-tensor views -- same results as the
+    oracle, bit for bit."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make(name)
+    orc = OracleRun(w)
+    dev = DeviceRun(w, layout="flat")
+    try:
+        for s in range(1, min(w.steps, 3) + 1):
+            scale = orc.st.scaler.scale
+            acc_o = orc.step()
+            acc_d = dev.step(scale, snapshot=True)
+            say("  step", s, compare_step(dev, orc, w, s, acc_d, acc_o))
+    finally:
+        dev.close()
+
+
+def test_whole_model_as_one_tensor(mp):
+    """A caller who flattens the whole model into one buffer per kind passes a one-tensor plan
+    (the chunk table then cuts one range): the update equals the per-tensor oracle."""
+    import torch
+    import inputs
+    from harness import OracleRun
+    w = configs.make("llama3-8B-small")
+    orc = OracleRun(w)
+    total = w.total
+    offs = np.cumsum([0] + w.numels[:-1])
+    bufs = {name: torch.zeros(total, dtype=torch.float32, device="cuda")
+            for name in ("acc", "master", "m", "v")}
+    w16 = torch.zeros(total, dtype=torch.bfloat16, device="cuda")
+    g16 = [torch.zeros(total, dtype=torch.bfloat16, device="cuda") for _ in range(w.k)]
+    for t, (o, n) in enumerate(zip(offs, w.numels)):
+        inputs.fill_dev_f32(bufs["master"][o:o + n], w.master_recipe(t))
+    plan = mp.mp_plan_create([total], mp.MP_BF16, [bufs["acc"]], [bufs["master"]], [bufs["m"]],
+                             [bufs["v"]], [w16])
+    sets = [mp.mp_gradset_create(plan, [g]) for g in g16]
+    st = mp.mp_state_create(mp.scaler_cfg(init_scale=1.0, enabled=False))
+    hp = mp.adamw_hparams(**w.hp)
+    try:
+        for s in range(1, 3):
+            orc.step()
+            for i in range(w.k):
+                for t, (o, n) in enumerate(zip(offs, w.numels)):
+                    inputs.fill_dev_u16(g16[i][o:o + n], w.grad_recipe(s, i, t), w.dtype)
+            wts = mp.mp_token_weights(w.token_counts(s))
+            for i in range(w.k - 1):
+                mp.mp_accumulate(plan, sets[i], wts[i], i == 0)
+            mp.mp_unscale_check_norm(plan, st, sets[-1], wts[-1], 0, w.max_norm)
+            mp.mp_adamw_step(plan, st, sets[-1], wts[-1], 0, hp)
+            mp.mp_scaler_update(st)
+            stats = mp.read_stats(st)
+            assert abs(stats["grad_norm"] - orc.st.norm) <= 1e-5 * orc.st.norm
+            same = np.float32(stats["grad_norm"]) == np.float32(orc.st.norm)
+            master = bufs["master"].cpu().numpy()
+            for t, (o, n) in enumerate(zip(offs, w.numels)):
+                if same:
+                    assert np.array_equal(master[o:o + n], orc.st.masters[t])
+                else:
+                    assert np.allclose(master[o:o + n], orc.st.masters[t], rtol=2e-6, atol=1e-9)
+            say("  step", s, "norm", stats["grad_norm"], "same bits", bool(same))
+    finally:
+        for g in sets:
+            mp.mp_gradset_destroy(g)
+        mp.mp_state_destroy(st)
+        mp.mp_plan_destroy(plan)

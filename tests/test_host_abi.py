@@ -141,3 +141,12 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_norm_finish(None, None, None, 1.0, None) == mp.MP_ERR_INVALID
     assert (L.mp_norm_partial(fake_state, fake_state, None, 1.0, 0, ctypes.c_void_p(0x10001), None)
             == mp.MP_ERR_INVALID)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asking for more exits with a message (no GPU touched)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
