@@ -521,17 +521,22 @@ __global__ __launch_bounds__(kBlock) void k_fp8_blocks16(const float* __restrict
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + threadIdx.x / kWave;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * (kBlock / kWave);
     for (int64_t base = wave * kWaveValues; base < n; base += waves * kWaveValues) {
+        F4 v[4];
+        bool live[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                          // all four loads in flight first
+            const int64_t e = base + j * kSlab + lane * kGroup;   // n is a multiple of 16
+            live[j] = e < n;
+            if (live[j]) v[j] = load_f4<true>(src + e, kGroup);
+            else v[j].v[0] = v[j].v[1] = v[j].v[2] = v[j].v[3] = 0.0f;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t e = base + j * kSlab + lane * kGroup;   // n is a multiple of 16
-            const bool live = e < n;
-            F4 v;
-            if (live) v = load_f4<true>(src + e, kGroup);
-            else v.v[0] = v.v[1] = v.v[2] = v.v[3] = 0.0f;
+            const int64_t e = base + j * kSlab + lane * kGroup;
             float amax = 0.0f;
 #pragma unroll
             for (int k = 0; k < kGroup; ++k) {
-                const float a = __builtin_fabsf(v.v[k]);
+                const float a = __builtin_fabsf(v[j].v[k]);
                 amax = a > amax ? a : amax;                        // a NaN never wins
             }
 #pragma unroll
@@ -541,8 +546,8 @@ __global__ __launch_bounds__(kBlock) void k_fp8_blocks16(const float* __restrict
             }
             float scale = amax / 448.0f;
             if (scale == 0.0f) scale = 1.0f;
-            if (live) {
-                *(MPK_GLOBAL uint32_t*)(codes + e) = pack_e4m3(v, scale);
+            if (live[j]) {
+                *(MPK_GLOBAL uint32_t*)(codes + e) = pack_e4m3(v[j], scale);
                 if ((lane & 3) == 0) scales[e / 16] = scale;
             }
         }
