@@ -191,6 +191,8 @@ def main():
     ap.add_argument("--layout", default="flat", choices=("tensor", "flat"),
                     help="one allocation per tensor, or one flat buffer per kind of array")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and replay it (launch-bound workloads)")
     ap.add_argument("--trace-steps", type=int, default=0,
                     help="time this many single steps after warm-up and print each")
     ap.add_argument("--no-extras", action="store_true",
@@ -249,7 +251,7 @@ def main():
 
     ev = {name: [] for name in ("accumulate", "norm", "adamw")}
 
-    def one_step(record):
+    def one_step_on(stream, record):
         def timed(name, fn):
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -270,6 +272,21 @@ def main():
                                                 stream))
         mp.mp_scaler_update(state, stream)
 
+    graph = None
+    if args.graph:
+        # the step is stream-ordered with no host sync: capture it once and replay it
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            one_step_on(torch.cuda.current_stream(), False)
+
+    def one_step(record):
+        if graph is not None:
+            graph.replay()
+        else:
+            one_step_on(stream, record)
+
     for _ in range(args.warmup):
         one_step(False)
     torch.cuda.synchronize()
@@ -287,7 +304,7 @@ def main():
     g1 = torch.cuda.Event(enable_timing=True)
     g0.record(stream)
     for _ in range(args.steps):
-        one_step(True)
+        one_step(False)
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -297,6 +314,12 @@ def main():
     log("stats after timing:", stats)
 
     bpp = bytes_per_param(k)
+    # per-kernel durations: the same number of eager steps again, with HIP events around every
+    # launch on the library's stream (kept out of the timed region above, whose host overhead
+    # they would inflate on small workloads, and impossible inside a replayed graph)
+    for _ in range(args.steps):
+        one_step_on(stream, True)
+    torch.cuda.synchronize()
     kernel_ms = {n: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None)
                  for n, v in ev.items()}
     adam_bytes = bpp["adamw"] * P
@@ -323,7 +346,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
         "config": {"workload": w.name, "params": P, "tensors": len(w.tensors), "k": k,
-                   "layout": args.layout,
+                   "layout": args.layout, "graph": bool(args.graph),
                    "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
                    "schedule": "k-1 accumulate passes, last micro-batch folded into norm and "
                                "AdamW passes",
