@@ -105,9 +105,9 @@ int device_cus(int device)
 // table stays small (16 B per chunk) on large ones.
 int32_t pick_chunk_elems(int64_t total, int grid_cap)
 {
-    int64_t target = total / (4ll * grid_cap);
+    int64_t target = total / (int64_t(MPK_CHUNKS_PER_SLOT) * grid_cap);
     int64_t ch = mpk::kBlockSlab;
-    while (ch < target && ch < (1ll << 16)) ch <<= 1;
+    while (ch < target && ch < MPK_MAX_CHUNK) ch <<= 1;
     return static_cast<int32_t>(ch);
 }
 

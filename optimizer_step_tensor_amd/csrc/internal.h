@@ -19,10 +19,13 @@
 namespace mpk {
 
 // Launch shape (compile-time).  The defaults were chosen by timing variants on
-// MI355X with the 8B-parameter tensor list resident: one block per chunk for the
-// accumulate and AdamW passes (the dispatcher then balances ragged chunks), 32
-// blocks per CU for the norm pass, and the nontemporal hint on every streamed
-// load and store (each byte is touched once per pass).
+// MI355X with the 1.3B, ragged 4096-tensor and 8B-parameter lists resident:
+// chunks of one block pass (2048 elements) with one block per chunk for the
+// accumulate and AdamW passes -- the blocks resident at any moment then sweep a
+// compact window of memory instead of thousands of separate streams, and the
+// dispatcher balances ragged chunks -- 32 blocks per CU for the norm pass,
+// each taking 4 consecutive chunks at a time, and the nontemporal hint on
+// every streamed load and store (each byte is touched once per pass).
 #ifndef MPK_GROUPS_PER_LANE
 #define MPK_GROUPS_PER_LANE 2      // groups of 4 elements per lane per block pass
 #endif
@@ -31,6 +34,15 @@ namespace mpk {
 #endif
 #ifndef MPK_NORM_BLOCKS_PER_CU
 #define MPK_NORM_BLOCKS_PER_CU 32  // norm grid: blocks per compute unit (fixed per plan)
+#endif
+#ifndef MPK_MAX_CHUNK
+#define MPK_MAX_CHUNK 2048         // largest chunk (elements); chunks are powers of two
+#endif
+#ifndef MPK_CHUNKS_PER_SLOT
+#define MPK_CHUNKS_PER_SLOT 4      // chunk size target: total / (this * 8 blocks per CU * CUs)
+#endif
+#ifndef MPK_NORM_CHUNK_GROUP
+#define MPK_NORM_CHUNK_GROUP 4     // consecutive chunks a norm block takes at a time
 #endif
 #ifndef MPK_NT_LOADS
 #define MPK_NT_LOADS 1             // nontemporal hint on streamed loads

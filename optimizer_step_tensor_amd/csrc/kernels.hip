@@ -256,7 +256,11 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
 {
     const float inv = st->inv_scale;
     double s = 0.0;
-    for (int64_t c = blockIdx.x; c < p.n_chunks; c += gridDim.x) {
+    // Blocks take groups of MPK_NORM_CHUNK_GROUP consecutive chunks, group b, b+G, ...
+    const int64_t n_groups = (p.n_chunks + MPK_NORM_CHUNK_GROUP - 1) / MPK_NORM_CHUNK_GROUP;
+    for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x)
+    for (int64_t c = grp * MPK_NORM_CHUNK_GROUP;
+         c < p.n_chunks && c < (grp + 1) * MPK_NORM_CHUNK_GROUP; ++c) {
         const Chunk ch = p.chunks[c];
         const float* acc = MODE == kLastOnly ? nullptr : p.tensors[ch.tensor].acc + ch.start;
         const uint16_t* g = MODE == kAccOnly ? nullptr : last[ch.tensor] + ch.start;

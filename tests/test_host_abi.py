@@ -96,10 +96,17 @@ def test_chunk_layout_covers_every_element_once(mp):
         _check_layout(mp, numel, int(rng.integers(1, 400)))
 
 
-def test_chunk_size_grows_with_the_model(mp):
-    small, _ = _check_layout(mp, [10_000], 256)
-    big, chunks = _check_layout(mp, [2 ** 33], 256)
-    assert small == 2048 and big == 65536 and len(chunks) == 2 ** 33 // 65536
+def test_chunk_count_at_full_size(mp):
+    """The 8B-parameter list: one chunk per 2048 elements of every tensor, ragged tails counted."""
+    import ctypes as C
+    from inputs import configs
+    numel = configs.make("llama3-8B").numels
+    ne = (C.c_int64 * len(numel))(*numel)
+    ch, nc = C.c_int32(), C.c_int64()
+    assert mp.lib().mp_chunk_layout(len(numel), ne, 256, C.byref(ch), C.byref(nc), None, None,
+                                    None, 0) == 0
+    assert nc.value == sum(-(-n // ch.value) for n in numel)
+    assert ch.value == 2048
 
 
 def test_validation_before_any_device_work(mp):
