@@ -1,6 +1,7 @@
 """Parity at the full sizes the benchmark times (needs an MI355X with ~210 GB free).
 
-The device runs the whole tensor list in the launch configuration bench.py uses;
+The device runs the whole tensor list in the launch configuration and memory layout
+bench.py uses (flattened buffers, per-tensor views);
 the oracle recomputes the global norm from regenerated inputs every step
 (streamed, all elements) and the update on sampled windows: the first and last
 512 elements of every tensor plus 64 seeded random windows of 4099 elements.
@@ -27,7 +28,7 @@ def test_full_size_sampled_parity(name, steps):
     assert torch.cuda.is_available()
     w = configs.make(name)
     say("full-size %s: %d tensors, %d params, k=%d" % (name, len(w.tensors), w.total, w.k))
-    dev = DeviceRun(w)
+    dev = DeviceRun(w, layout="flat")
     so = StreamedOracle(w, sample_windows(w), log=say)
     try:
         for s in range(1, steps + 1):
