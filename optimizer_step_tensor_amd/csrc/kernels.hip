@@ -712,9 +712,10 @@ hipError_t launch_fp8_blocks(const float* src, uint8_t* codes, float* scales, in
     const int64_t nblocks = n / block;
     if (nblocks == 0) return hipSuccess;
     if (block == 16) {
+        // one wave pass per wave (timed best on MI355X, like the one-block-per-chunk passes)
         int64_t waves = (n + 1023) / 1024;
         int64_t grid = (waves + kBlock / kWave - 1) / (kBlock / kWave);
-        if (grid > 16384) grid = 16384;
+        if (grid > (int64_t(1) << 30)) grid = int64_t(1) << 30;
         k_fp8_blocks16<<<static_cast<unsigned>(grid), kBlock, 0, s>>>(src, codes, scales, n);
     } else {
         k_fp8_blocks<<<elementwise_grid(nblocks), kBlock, 0, s>>>(src, codes, scales, nblocks, block);
