@@ -154,3 +154,86 @@ def test_fp16_extremes_with_scaler(mp):
               interval=2)
     rep = run_both(mp, mp.MP_FP16, masters, grads, counts=[100], steps=3, scaler=sc)
     assert [r[0] for r in rep] == [0, 1, 0] and [r[2] for r in rep] == [16.0, 8.0, 8.0]
+
+
+
+def test_no_writes_outside_the_tensors(mp):
+    """Ragged tensors laid out with 64-element guard gaps that hold a canary pattern: after
+    accumulation, the norm, AdamW, the scaler and the FP8 block cast, every guard is intact
+    (no ragged tail writes past its tensor) and every element inside a tensor was written."""
+    import torch
+    from inputs import configs
+    w = configs.make("ragged-4096-small")
+    numels = w.numels[:600] + [1, 2, 3, 5, 16, 2047, 2049, 4096, 4097]
+    gap = 64
+    offs, total = [], 0
+    for n in numels:
+        offs.append(total)
+        total += (n + 15) // 16 * 16 + gap          # 16-element starts: FP8 codes need 16 B
+    canary32 = 0x7FA5A5A5                           # a NaN payload no kernel writes
+    canary16 = 0x7FA5
+
+    def buf32():
+        return torch.full((total,), canary32, dtype=torch.int32, device="cuda").view(torch.float32)
+
+    def buf16():
+        return torch.full((total,), canary16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+    bufs = {k: buf32() for k in ("acc", "master", "m", "v")}
+    w16 = buf16()
+    grads = [buf16() for _ in range(2)]
+
+    def views(b):
+        return [b[o:o + n] for o, n in zip(offs, numels)]
+
+    for name in ("master", "m", "v"):
+        for x in views(bufs[name]):
+            x.fill_(0.25 if name == "master" else 0.0)
+    for g in grads:
+        for x in views(g):
+            x.fill_(1e-3)
+    plan = mp.mp_plan_create(numels, mp.MP_BF16, views(bufs["acc"]), views(bufs["master"]),
+                             views(bufs["m"]), views(bufs["v"]), views(w16))
+    sets = [mp.mp_gradset_create(plan, views(g)) for g in grads]
+    st = mp.mp_state_create(mp.scaler_cfg(init_scale=1.0, enabled=False))
+    codes = torch.full((total,), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((total // 16 + 64,), canary32, dtype=torch.int32,
+                        device="cuda").view(torch.float32)
+    try:
+        for _ in range(2):
+            mp.mp_accumulate(plan, sets[0], 0.5, 1)
+            mp.mp_unscale_check_norm(plan, st, sets[1], 0.5, 0, 1.0)
+            mp.mp_adamw_step(plan, st, sets[1], 0.5, 0, mp.adamw_hparams())
+            mp.mp_scaler_update(st)
+        cast = [(o, n) for o, n in zip(offs, numels) if n % 16 == 0]
+        assert len(cast) >= 3
+        for o, n in cast:
+            mp.mp_cast_fp8_blocks(bufs["master"][o:].data_ptr(), codes[o:].data_ptr(),
+                                  scales[o // 16:].data_ptr(), n, 16)
+        torch.cuda.synchronize()
+        inside = np.zeros(total, bool)
+        for o, n in zip(offs, numels):
+            inside[o:o + n] = True
+        for name, b in bufs.items():
+            got = b.view(torch.int32).cpu().numpy()
+            assert (got[~inside] == canary32).all(), name
+            assert (got[inside] != canary32).all(), name
+        got16 = w16.view(torch.int16).cpu().numpy()
+        assert (got16[~inside] == canary16).all() and (got16[inside] != canary16).all()
+        for g in grads:                                   # gradients are read, never written
+            assert (g.view(torch.int16).cpu().numpy()[~inside] == canary16).all()
+        cast_in = np.zeros(total, bool)
+        sc_in = np.zeros(scales.numel(), bool)
+        for o, n in cast:
+            cast_in[o:o + n] = True
+            sc_in[o // 16:o // 16 + n // 16] = True
+        assert (codes.cpu().numpy()[~cast_in] == 0x5A).all()
+        got_sc = scales.view(torch.int32).cpu().numpy()
+        assert (got_sc[~sc_in] == canary32).all() and (got_sc[sc_in] != canary32).all()
+        stats = mp.read_stats(st)
+        assert stats["found_inf"] == 0 and stats["skipped_total"] == 0
+    finally:
+        for g in sets:
+            mp.mp_gradset_destroy(g)
+        mp.mp_state_destroy(st)
+        mp.mp_plan_destroy(plan)
