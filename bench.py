@@ -11,7 +11,7 @@ Prints ONE JSON line: params/s of the whole step (value), the roofline of the
 dominant kernel (the AdamW pass, timed live with HIP events on the stream it
 runs on), and the oracle timed on the host's cores over a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--graph] [--gpus 1]
 """
 import argparse
 import hashlib
@@ -80,9 +80,23 @@ def cpu_baseline(w, seconds_hint=20.0):
     st.scaler_update()
     dt_s = time.perf_counter() - t0
     n_sample = sum(p[2] for p in pieces)
+    # the same oracle on one thread, over one 16M-element segment
+    j = max(range(len(pieces)), key=lambda i: pieces[i][2])
+    one = oracle.OracleStep(dt, [masters[j].copy()], [np.zeros(masters[j].size, np.uint16)],
+                            with_acc=w.k > 1, threads=1)
+    t1 = time.perf_counter()
+    for i in range(w.k - 1):
+        one.accumulate([grads[i][j]], weights[i], i == 0)
+    one.unscale_check_norm([grads[-1][j]], weights[-1], w.k == 1, w.max_norm)
+    one.adamw_step([grads[-1][j]], weights[-1], w.k == 1, **w.hp)
+    one.scaler_update()
+    dt_1 = time.perf_counter() - t1
     return {"value": n_sample / dt_s, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": "%d params (%d tensors of the first layer, %d segments), k=%d, one full step, "
-                      "%.1f s" % (n_sample, len(sample), len(pieces), w.k, dt_s)}
+                      "%.1f s" % (n_sample, len(sample), len(pieces), w.k, dt_s),
+            "single_thread": {"value": masters[j].size / dt_1, "unit": "params/s",
+                              "sample": "one segment (%d params), %.2f s"
+                                        % (masters[j].size, dt_1)}}
 
 
 def kernel_sha():
@@ -128,6 +142,14 @@ def run_extras(mp, torch, w, model, g16, hp, weights, stream):
       multiples of 8 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
     out = {}
     P, k = w.total, w.k
+    # context for the roofline: the runtime's own device-to-device copy of 4 GiB
+    a = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms = time_launches(torch, stream, lambda: b.copy_(a), 5)
+    out["device_copy"] = {"bytes_read": 4 << 30, "bytes_written": 4 << 30, "ms": ms,
+                          "GBps": 2 * (4 << 30) / ms / 1e6,
+                          "frac": 2 * (4 << 30) / ms / 1e6 / HBM_PEAK_GBPS}
+    del a, b
     big = max(w.numels)
     codes = torch.empty(big, dtype=torch.uint8, device="cuda")
     scales = torch.empty(big // 16 + 1, dtype=torch.float32, device="cuda")
@@ -199,6 +221,10 @@ def main():
                     help="skip the FP8 block cast and one ZeRO-8 rank's slice")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (for counter calibration)")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 1 GiB scratch buffer before every timed step (evicts the "
+                         "state of small workloads from the last-level cache) and time each step "
+                         "with its own events")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -299,26 +325,44 @@ def main():
             b.record(stream)
             b.synchronize()
             log("trace step %d: %.3f ms" % (i, a.elapsed_time(b)))
-    t0 = time.perf_counter()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.steps):
-        one_step(False)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = g0.elapsed_time(g1)
-    ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
+    # eager steps carry HIP events around every launch, on the stream the library launches
+    # on, inside the timed region; a replayed graph cannot, so after a graph run the same
+    # number of eager steps is timed with events outside it
+    record = graph is None
+    if args.cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        step_ms = []
+        for _ in range(args.steps):
+            flush.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            one_step(record)
+            b.record(stream)
+            b.synchronize()
+            step_ms.append(a.elapsed_time(b))
+        ms_per_step = sum(step_ms) / len(step_ms)
+        del flush
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            one_step(record)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = g0.elapsed_time(g1)
+        ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
     stats = mp.read_stats(state)
     log("stats after timing:", stats)
 
     bpp = bytes_per_param(k)
-    # per-kernel durations: the same number of eager steps again, with HIP events around every
-    # launch on the library's stream (kept out of the timed region above, whose host overhead
-    # they would inflate on small workloads, and impossible inside a replayed graph)
-    for _ in range(args.steps):
-        one_step_on(stream, True)
+    if not record:
+        for _ in range(args.steps):
+            one_step_on(stream, True)
     torch.cuda.synchronize()
     kernel_ms = {n: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None)
                  for n, v in ev.items()}
@@ -347,6 +391,9 @@ def main():
         "data": "synthetic (seeded counter-based generator, inputs resident in HBM)",
         "config": {"workload": w.name, "params": P, "tensors": len(w.tensors), "k": k,
                    "layout": args.layout, "graph": bool(args.graph),
+                   "cache": "cold (1 GiB overwritten before each step)" if args.cold else "warm",
+                   "kernel_events": "inside the timed region" if record else
+                                    "eager steps after the timed graph replays",
                    "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
                    "schedule": "k-1 accumulate passes, last micro-batch folded into norm and "
                                "AdamW passes",
