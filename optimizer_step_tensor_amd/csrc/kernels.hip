@@ -6,9 +6,10 @@
 // of 4 consecutive elements 256 elements apart, so every fp32 load or store
 // instruction of a wave moves one contiguous 1 KiB line run (16 B per lane)
 // and every 16-bit one a contiguous 512 B run.  Only the last partial group
-// of a tensor takes the scalar path.  Blocks take chunks b, b+G, b+2G, ... so
-// the assignment of elements to lanes is fixed, which makes the norm's
-// reduction order -- and its bits -- the same on every run.
+// of a tensor takes the scalar path.  Every block's share of chunks is fixed by
+// its index and the grid, so the assignment of elements to lanes is fixed,
+// which makes the norm's reduction order -- and its bits -- the same on every
+// run.
 //
 // Arithmetic: compiled with -ffp-contract=off and correctly rounded fp32
 // division and square root, so every operation below is one IEEE-754 binary32
@@ -148,6 +149,19 @@ __device__ __forceinline__ void store_h4(uint16_t* p, const H4& r, int nv)
     }
 }
 
+// The chunk block b of a G-block grid starts at.  Workgroup b runs on XCD
+// b mod 8; this renumbering gives each XCD MPK_XCD_SPAN consecutive chunks per
+// turn of 8 * MPK_XCD_SPAN blocks.  It permutes 0..G-1: blocks of the last,
+// incomplete turn keep their own number.
+__device__ __forceinline__ int64_t xcd_first_chunk(int64_t b, int64_t G)
+{
+    constexpr int64_t span = MPK_XCD_SPAN;
+    constexpr int64_t turn = span * kXcds;
+    if (span <= 1 || b >= (G / turn) * turn) return b;
+    const int64_t t = b / turn, within = b % turn;
+    return t * turn + (within % kXcds) * span + within / kXcds;
+}
+
 // Run pass(full, base) over a chunk of `len` elements: every complete
 // 2048-element block pass with full = true_type (no bounds checks at all),
 // then the one partial pass, if any, with full = false_type.
@@ -211,7 +225,8 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
                                                        const uint16_t* const* __restrict__ g16,
                                                        float w)
 {
-    for (int64_t c = blockIdx.x; c < p.n_chunks; c += gridDim.x) {
+    for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
+         c += gridDim.x) {
         const Chunk ch = p.chunks[c];
         float* acc = p.tensors[ch.tensor].acc + ch.start;
         const uint16_t* g = g16[ch.tensor] + ch.start;
@@ -368,7 +383,8 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
     const float b1 = a.beta1, b2 = a.beta2;
     const float ob1 = 1.0f - b1, ob2 = 1.0f - b2;
     const float eps = a.eps, lr = a.lr;
-    for (int64_t c = blockIdx.x; c < p.n_chunks; c += gridDim.x) {
+    for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
+         c += gridDim.x) {
         const Chunk ch = p.chunks[c];
         const TensorDesc td = p.tensors[ch.tensor];
         const float lam = a.weight_decay * td.wd_mult;
