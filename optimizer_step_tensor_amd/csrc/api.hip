@@ -23,10 +23,10 @@ struct mp_plan {
     int64_t n_chunks;
     int32_t chunk_elems;
     int grid;                 // blocks of the accumulate and AdamW passes
-    int norm_grid;            // blocks of the norm pass (= partial sums)
+    int norm_grid;            // blocks of the norm pass (= first-stage partial sums)
     TensorDesc* d_tensors;
     Chunk* d_chunks;
-    double* d_partials;       // norm_grid entries
+    double* d_partials;       // norm_grid first-stage + kNormStage2 second-stage sums
     // call-order bookkeeping: mp_adamw_step must follow mp_unscale_check_norm (or
     // mp_norm_partial + mp_norm_finish)
     bool partial_pending;
@@ -276,11 +276,12 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
     p->n_chunks = static_cast<int64_t>(chunks.size());
     p->chunk_elems = ch;
     p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
-    p->norm_grid = static_cast<int>(std::min<int64_t>(p->n_chunks, cus * MPK_NORM_BLOCKS_PER_CU));
-    std::vector<double> zeros(p->norm_grid, 0.0);
+    p->norm_grid = p->grid;
+    // every partial sum is written by its block before any kernel reads it
+    const size_t partial_bytes = (static_cast<size_t>(p->norm_grid) + mpk::kNormStage2) * sizeof(double);
     if ((e = upload(&p->d_tensors, tensors)) != hipSuccess ||
         (e = upload(&p->d_chunks, chunks)) != hipSuccess ||
-        (e = upload(&p->d_partials, zeros)) != hipSuccess) {
+        (e = hipMalloc(reinterpret_cast<void**>(&p->d_partials), partial_bytes)) != hipSuccess) {
         mp_plan_destroy(p);
         return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
                                         : hip_fail(e, "plan upload");

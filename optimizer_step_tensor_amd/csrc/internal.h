@@ -20,16 +20,15 @@ namespace mpk {
 
 // Launch shape (compile-time).  The defaults were chosen by timing variants on
 // MI355X with the 1.3B, ragged 4096-tensor and 8B-parameter lists resident:
-// chunks of one block pass (2048 elements) with one block per chunk for the
-// accumulate and AdamW passes -- the blocks resident at any moment then sweep a
-// compact window of memory instead of thousands of separate streams, and the
-// dispatcher balances ragged chunks -- 32 blocks per CU for the norm pass,
-// each taking 4 consecutive chunks at a time, and the nontemporal hint on
-// every streamed load and store (each byte is touched once per pass).  The
-// dispatcher hands consecutive workgroups to the 8 XCDs in turn; the accumulate
-// and AdamW passes renumber their blocks so that each XCD takes runs of 64
-// consecutive chunks (512 KiB of every fp32 array) rather than every 8th chunk,
-// which made the whole step 2-3.5% faster on all three lists.
+// chunks of one block pass (2048 elements) with one block per chunk for every
+// streaming pass -- the blocks resident at any moment then sweep a compact
+// window of memory instead of thousands of separate streams, and the
+// dispatcher balances ragged chunks -- and the nontemporal hint on every
+// streamed load and store (each byte is touched once per pass).  The
+// dispatcher hands consecutive workgroups to the 8 XCDs in turn; the passes
+// renumber their blocks so that each XCD takes runs of 64 consecutive chunks
+// (512 KiB of every fp32 array) rather than every 8th chunk, which made the
+// accumulate and AdamW passes 2-3.5% faster and the norm pass 2-8% faster.
 #ifndef MPK_XCD_SPAN
 #define MPK_XCD_SPAN 64            // consecutive chunks per XCD turn; 1: no renumbering
 #endif
@@ -37,19 +36,13 @@ namespace mpk {
 #define MPK_GROUPS_PER_LANE 2      // groups of 4 elements per lane per block pass
 #endif
 #ifndef MPK_ELEM_BLOCKS_PER_CU
-#define MPK_ELEM_BLOCKS_PER_CU 0   // accumulate / AdamW grid cap per CU; 0: one block per chunk
-#endif
-#ifndef MPK_NORM_BLOCKS_PER_CU
-#define MPK_NORM_BLOCKS_PER_CU 32  // norm grid: blocks per compute unit (fixed per plan)
+#define MPK_ELEM_BLOCKS_PER_CU 0   // grid cap per CU of the streaming passes; 0: one block per chunk
 #endif
 #ifndef MPK_MAX_CHUNK
 #define MPK_MAX_CHUNK 2048         // largest chunk (elements); chunks are powers of two
 #endif
 #ifndef MPK_CHUNKS_PER_SLOT
 #define MPK_CHUNKS_PER_SLOT 4      // chunk size target: total / (this * 8 blocks per CU * CUs)
-#endif
-#ifndef MPK_NORM_CHUNK_GROUP
-#define MPK_NORM_CHUNK_GROUP 4     // consecutive chunks a norm block takes at a time
 #endif
 #ifndef MPK_NT_LOADS
 #define MPK_NT_LOADS 1             // nontemporal hint on streamed loads
@@ -61,6 +54,7 @@ namespace mpk {
 constexpr int kBlock = 256;                          // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
 constexpr int kXcds = 8;                             // XCDs per MI355X
+constexpr int kNormStage2 = 256;                     // second-stage sums of the norm
 constexpr int kGroup = 4;                            // elements per 16-byte fp32 vector
 constexpr int kGroupsPerLane = MPK_GROUPS_PER_LANE;
 constexpr int kWaveSlab = kWave * kGroup * kGroupsPerLane;   // 512 elements per wave pass

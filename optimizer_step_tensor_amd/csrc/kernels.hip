@@ -257,10 +257,10 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
 }
 
 // ---------------------------------------------------------------------------
-// Unscale + sum of squares, first stage: one binary64 partial per block.
-// An inf or NaN gradient makes the sum inf or NaN; finite fp32 squares cannot
-// overflow binary64 for any element count a device can hold, so the overflow
-// flag is exactly "the sum is not finite".
+// Unscale + sum of squares, first stage: one binary64 partial per block (one
+// block per chunk by default).  An inf or NaN gradient makes the sum inf or
+// NaN; finite fp32 squares cannot overflow binary64 for any element count a
+// device can hold, so the overflow flag is exactly "the sum is not finite".
 // ---------------------------------------------------------------------------
 template <int DT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
@@ -271,11 +271,8 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
 {
     const float inv = st->inv_scale;
     double s = 0.0;
-    // Blocks take groups of MPK_NORM_CHUNK_GROUP consecutive chunks, group b, b+G, ...
-    const int64_t n_groups = (p.n_chunks + MPK_NORM_CHUNK_GROUP - 1) / MPK_NORM_CHUNK_GROUP;
-    for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x)
-    for (int64_t c = grp * MPK_NORM_CHUNK_GROUP;
-         c < p.n_chunks && c < (grp + 1) * MPK_NORM_CHUNK_GROUP; ++c) {
+    for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
+         c += gridDim.x) {
         const Chunk ch = p.chunks[c];
         const float* acc = MODE == kLastOnly ? nullptr : p.tensors[ch.tensor].acc + ch.start;
         const uint16_t* g = MODE == kAccOnly ? nullptr : last[ch.tensor] + ch.start;
@@ -311,7 +308,21 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
 }
 
-// Second stage: fixed-order sum of the partials, norm, clip coefficient
+// Second stage: block j sums the j-th of `gridDim.x` contiguous ranges of the n
+// first-stage partials, each lane a fixed strided subset, then the block tree.
+__global__ __launch_bounds__(kBlock) void k_norm_stage2(const double* __restrict__ partials,
+                                                        int64_t n, double* __restrict__ out)
+{
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t hi = lo + per < n ? lo + per : n;
+    double s = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) s += partials[i];
+    const double total = block_sum(s);
+    if (threadIdx.x == 0) out[blockIdx.x] = total;
+}
+
+// Last stage: fixed-order sum of the second-stage sums, norm, clip coefficient
 // ("Megatron Internals III", section 9).
 __global__ __launch_bounds__(kBlock) void k_norm_finish(const double* __restrict__ partials,
                                                         int n, float max_norm,
@@ -660,7 +671,9 @@ hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last,
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    k_norm_finish<<<1, kBlock, 0, s>>>(partials, grid, max_norm, st);
+    const int n2 = grid < kNormStage2 ? grid : kNormStage2;
+    k_norm_stage2<<<n2, kBlock, 0, s>>>(partials, grid, partials + grid);
+    k_norm_finish<<<1, kBlock, 0, s>>>(partials + grid, n2, max_norm, st);
     return hipGetLastError();
 }
 
@@ -680,7 +693,9 @@ hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* cons
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    k_norm_reduce<<<1, kBlock, 0, s>>>(partials, grid, out);
+    const int n2 = grid < kNormStage2 ? grid : kNormStage2;
+    k_norm_stage2<<<n2, kBlock, 0, s>>>(partials, grid, partials + grid);
+    k_norm_reduce<<<1, kBlock, 0, s>>>(partials + grid, n2, out);
     return hipGetLastError();
 }
 
