@@ -9,7 +9,9 @@ region and stay resident in HBM.
 
 Prints ONE JSON line: params/s of the whole step (value), the roofline of the
 dominant kernel (the AdamW pass, timed live with HIP events on the stream it
-runs on), and the oracle timed on the host's cores over a bounded sample.
+runs on), the fused step (norm + AdamW + scaler, the two passes over the final
+gradient) in GB/s, and the oracle timed on the host's cores over a bounded
+sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--graph] [--gpus 1]
 """
@@ -39,7 +41,7 @@ def bytes_per_param(k):
     return {
         "accumulate_first": 2 + 4,            # read g16, write acc
         "accumulate": 2 + 4 + 4,              # read g16 + acc, write acc
-        "norm": 4 + 2,                        # read acc + last g16
+        "norm": (4 if k > 1 else 0) + 2,      # read acc (k > 1) + last g16
         # read acc (k > 1), last g16, w, m, v; write w, m, v, w16
         "adamw": (4 if k > 1 else 0) + 2 + 4 + 4 + 4 + (4 + 4 + 4 + 2),
         "step": (6 + 10 * (k - 2) + 6 + 32) if k >= 2 else (2 + 2 + 4 * 3 + 12 + 2),
@@ -275,7 +277,7 @@ def main():
         log("copy calibration: %d bytes read, %d bytes written" % (4 * n, 4 * n))
         del a, b
 
-    ev = {name: [] for name in ("accumulate", "norm", "adamw")}
+    ev = {name: [] for name in ("accumulate", "norm", "adamw", "fused")}
 
     def one_step_on(stream, record):
         def timed(name, fn):
@@ -292,11 +294,18 @@ def main():
         for i in range(k - 1):
             timed("accumulate", lambda i=i: mp.mp_accumulate(plan, sets[i], weights[i], i == 0,
                                                              stream))
+        if record:                            # the fused step: norm + AdamW + scaler
+            f0 = torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
         timed("norm", lambda: mp.mp_unscale_check_norm(plan, state, sets[-1], weights[-1], lif,
                                                        w.max_norm, stream))
         timed("adamw", lambda: mp.mp_adamw_step(plan, state, sets[-1], weights[-1], lif, hp,
                                                 stream))
         mp.mp_scaler_update(state, stream)
+        if record:
+            f1 = torch.cuda.Event(enable_timing=True)
+            f1.record(stream)
+            ev["fused"].append((f0, f1))
 
     graph = None
     if args.graph:
@@ -369,7 +378,11 @@ def main():
     adam_bytes = bpp["adamw"] * P
     achieved = adam_bytes / (kernel_ms["adamw"] * 1e-3) / 1e9
     step_bytes = bpp["step"] * P
+    fused_bpp = bpp["norm"] + bpp["adamw"]
+    fused_gbps = fused_bpp * P / kernel_ms["fused"] / 1e6
     log("per-launch ms:", {n: round(x, 4) for n, x in kernel_ms.items() if x})
+    log("fused step (norm + AdamW + scaler): %.3f ms, %.1f GB/s (%.1f%% of %.0f)"
+        % (kernel_ms["fused"], fused_gbps, fused_gbps / HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
     log("step: %.3f ms, %.1f GB/s algorithmic (%.1f%% of %.0f)"
         % (ms_per_step, step_bytes / ms_per_step / 1e6, step_bytes / ms_per_step / 1e6 /
            HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
@@ -408,6 +421,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "bytes_per_param": bpp["adamw"],
                      "traffic": traffic},
+        "fused_step": {"passes": "unscale/overflow/norm + AdamW/RNE cast + scaler",
+                       "bytes_per_param": fused_bpp, "ms": kernel_ms["fused"],
+                       "GBps": fused_gbps, "hbm_frac": fused_gbps / HBM_PEAK_GBPS},
         "cpu_baseline": None,
         "extras": extras,
     }
