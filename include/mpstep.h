@@ -36,7 +36,7 @@
  *  - The library owns plans, gradsets and states.  It allocates device memory
  *    only in the *_create calls, never in the hot calls.
  *  - Objects are bound to the HIP device that was current at creation; make it
- *    current before calling a hot entry point.
+ *    current before calling a hot entry point (else MP_ERR_INVALID).
  *  - `stream` is a hipStream_t passed as void* (NULL: the null stream).  Hot
  *    calls only enqueue work on it and return; results reach the host through
  *    mp_state_read.
@@ -208,7 +208,10 @@ mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale);
  * where widen is the exact 16-bit -> fp32 conversion and weight = n_i/N from
  * mp_token_weights (finite, > 0).  `first` starts a new logical update and
  * discards whatever the buffer held (the gradients of a skipped step).
- * MP_ERR_INVALID if the plan has no accumulators. */
+ * MP_ERR_INVALID if the plan has no accumulators.  The call changes the
+ * gradient a preceding mp_unscale_check_norm / mp_norm_partial measured, so the
+ * next mp_adamw_step on this plan returns MP_ERR_ORDER until the norm is
+ * measured again. */
 mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
                         mp_stream stream);
 
@@ -267,7 +270,11 @@ mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, 
  * "Dynamic scaling"; "Megatron Internals III", section 5): skipped = found_inf;
  * on overflow S = max(S*backoff, min_scale) and the count restarts; on a clean
  * step the count grows and, on reaching `interval`, S = min(S*growth,
- * max_scale) and the count restarts.  A disabled scaler keeps S. */
+ * max_scale) and the count restarts.  A disabled scaler keeps S.  Exactly one
+ * call per measurement: it must follow mp_unscale_check_norm (or
+ * mp_norm_finish) on this state, with no mp_scaler_update in between, else
+ * MP_ERR_ORDER (a second call would count the same clean step twice).
+ * mp_state_import leaves no measurement pending. */
 mp_status mp_scaler_update(mp_state* state, mp_stream stream);
 
 /* Elementwise casts with the step's conversions: dst = round-to-nearest-even

@@ -45,6 +45,9 @@ struct mp_gradset {
 struct mp_state {
     int device;
     DevState* d;
+    // an overflow/norm decision was measured into this state and the scaler has
+    // not consumed it yet (mp_scaler_update must follow a measurement)
+    bool decision_pending;
 };
 
 namespace {
@@ -161,6 +164,26 @@ int grad_mode(const mp_gradset* last, int32_t last_is_first)
 {
     if (last == nullptr) return mpk::kAccOnly;
     return last_is_first ? mpk::kLastOnly : mpk::kAccPlusLast;
+}
+
+// Plans and states are bound to the device current at their creation; a hot
+// call made with another device current would launch on the wrong GPU.
+mp_status check_device(int device, const char* what)
+{
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != device)
+        return fail(MP_ERR_INVALID, "%s was created on device %d but device %d is current", what,
+                    device, cur);
+    return MP_OK;
+}
+
+mp_status check_devices(const mp_plan* plan, const mp_state* state)
+{
+    mp_status st = plan ? check_device(plan->device, "the plan") : MP_OK;
+    if (st == MP_OK && state) st = check_device(state->device, "the state");
+    return st;
 }
 
 mp_status check_last(const mp_plan* plan, const mp_gradset* last, float w_last,
@@ -480,6 +503,7 @@ mp_status mp_state_import(mp_state* state, const void* blob, size_t blob_bytes, 
     hipError_t e = hipMemcpyAsync(state->d, &d, sizeof d, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);   // `d` lives on this stack frame
     if (e != hipSuccess) return hip_fail(e, "state import");
+    state->decision_pending = false;                    // the blob is a state between steps
     return ok();
 }
 
@@ -497,9 +521,14 @@ mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int3
     if (g16->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
     if (!plan->has_acc) return fail(MP_ERR_INVALID, "the plan has no accumulators");
     if (!std::isfinite(weight) || !(weight > 0.0f)) return fail(MP_ERR_INVALID, "weight must be finite and > 0");
+    mp_status st = check_devices(plan, nullptr);
+    if (st != MP_OK) return st;
     hipError_t e = mpk::launch_accumulate(view(plan), plan->grid, g16->d_ptrs, weight, first != 0,
                                           plan->dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+    // the buffers changed: a norm measured before this no longer describes them
+    plan->partial_pending = false;
+    plan->norm_pending = false;
     return ok();
 }
 
@@ -511,10 +540,13 @@ mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset
     mp_status st = check_last(plan, last, w_last, last_is_first);
     if (st != MP_OK) return st;
     if (std::isnan(max_norm) || std::isinf(max_norm)) return fail(MP_ERR_INVALID, "max_norm must be finite");
+    st = check_devices(plan, state);
+    if (st != MP_OK) return st;
     hipError_t e = mpk::launch_norm(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr, w_last,
                                     grad_mode(last, last_is_first), plan->dtype, plan->d_partials,
                                     max_norm, state->d, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm launch");
+    state->decision_pending = true;
     plan->partial_pending = false;
     plan->norm_pending = true;
     plan->norm_state = state;
@@ -531,6 +563,7 @@ mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last
     if (partial_out == nullptr || (reinterpret_cast<uintptr_t>(partial_out) & 7u) != 0)
         return fail(MP_ERR_INVALID, "partial_out must be an 8-byte aligned device pointer");
     mp_status st = check_last(plan, last, w_last, last_is_first);
+    if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
     hipError_t e = mpk::launch_norm_partial(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr,
                                             w_last, grad_mode(last, last_is_first), plan->dtype,
@@ -557,8 +590,11 @@ mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, fl
     if (!plan->partial_pending || plan->norm_state != state)
         return fail(MP_ERR_ORDER, "mp_norm_finish must follow mp_norm_partial on the same plan "
                                   "and state");
+    mp_status st = check_devices(plan, state);
+    if (st != MP_OK) return st;
     hipError_t e = mpk::launch_norm_apply(sumsq, max_norm, state->d, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm finish launch");
+    state->decision_pending = true;
     plan->partial_pending = false;
     plan->norm_pending = true;
     return ok();
@@ -577,6 +613,8 @@ mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, 
                              plan->norm_last_is_first != (last_is_first ? 1 : 0))))
         return fail(MP_ERR_ORDER, "mp_adamw_step must follow mp_unscale_check_norm on the same "
                                   "plan and state, with the same last micro-batch arguments");
+    st = check_devices(plan, state);
+    if (st != MP_OK) return st;
     mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
     hipError_t e = mpk::launch_adamw(view(plan), plan->grid, last ? last->d_ptrs : nullptr, w_last,
                                      grad_mode(last, last_is_first), plan->dtype, a, state->d,
@@ -589,8 +627,14 @@ mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, 
 mp_status mp_scaler_update(mp_state* state, mp_stream stream)
 {
     if (state == nullptr) return fail(MP_ERR_INVALID, "state is NULL");
+    if (!state->decision_pending)
+        return fail(MP_ERR_ORDER, "mp_scaler_update must follow mp_unscale_check_norm (or "
+                                  "mp_norm_finish) on this state, once per measured step");
+    mp_status st = check_devices(nullptr, state);
+    if (st != MP_OK) return st;
     hipError_t e = mpk::launch_scaler(state->d, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "scaler launch");
+    state->decision_pending = false;
     return ok();
 }
 

@@ -151,6 +151,9 @@ def test_call_order_and_argument_errors(mp):
         with pytest.raises(mp.MpError) as e:
             mp.mp_adamw_step(plan, st, None, 1.0, 0, dev.hp)
         assert e.value.status == mp.MP_ERR_ORDER
+        with pytest.raises(mp.MpError) as e:           # no measured step to decide on
+            mp.mp_scaler_update(st)
+        assert e.value.status == mp.MP_ERR_ORDER
         mp.mp_unscale_check_norm(plan, st, g, 0.5, 0, 1.0)
         with pytest.raises(mp.MpError) as e:           # different last micro-batch weight
             mp.mp_adamw_step(plan, st, g, 0.25, 0, dev.hp)
@@ -169,6 +172,20 @@ def test_call_order_and_argument_errors(mp):
         with pytest.raises(mp.MpError) as e:
             mp.mp_state_create(mp.scaler_cfg(init_scale=3.0))
         assert e.value.status == mp.MP_ERR_INVALID
+        # an accumulation after the norm changes what the norm measured
+        mp.mp_unscale_check_norm(plan, st, g, 0.5, 0, 1.0)
+        mp.mp_accumulate(plan, g, 0.5, 1)
+        with pytest.raises(mp.MpError) as e:
+            mp.mp_adamw_step(plan, st, g, 0.5, 0, dev.hp)
+        assert e.value.status == mp.MP_ERR_ORDER
+        # one scaler decision per measured step
+        mp.mp_scaler_update(st)
+        with pytest.raises(mp.MpError) as e:
+            mp.mp_scaler_update(st)
+        assert e.value.status == mp.MP_ERR_ORDER
+        mp.mp_unscale_check_norm(plan, st, g, 0.5, 0, 1.0)
+        mp.mp_adamw_step(plan, st, g, 0.5, 0, dev.hp)
+        mp.mp_scaler_update(st)
     finally:
         dev.close()
 
