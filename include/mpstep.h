@@ -74,6 +74,7 @@ typedef enum { MP_BF16 = 0, MP_FP16 = 1 } mp_dtype16;
 typedef struct mp_plan mp_plan;        /* tensor list + chunk table (device) */
 typedef struct mp_gradset mp_gradset;  /* one micro-batch's gradient pointers (device) */
 typedef struct mp_state mp_state;      /* loss scale, optimizer clock, step results (device) */
+typedef struct mp_fp8set mp_fp8set;    /* per-tensor FP8 outputs of the fused AdamW (device) */
 typedef void* mp_stream;               /* hipStream_t */
 
 /* Dynamic loss scaler ("Mixed precision ...", section 2 "Dynamic scaling";
@@ -299,6 +300,28 @@ mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dty
  * aligned, scales 4-byte aligned; n/block scales are written. */
 mp_status mp_cast_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n,
                              int32_t block, mp_stream stream);
+
+/* FP8 outputs of selected tensors of a plan, for mp_adamw_step_fp8 ("Chapter
+ * 41 Training at Scale", section 41.5: selected tensors stored or
+ * communicated in FP8 with one scale per block).  For tensor i either both
+ * codes[i] (numel[i] bytes, 16-byte aligned) and scales[i] (numel[i]/16
+ * floats, 4-byte aligned) are device pointers the caller owns, or both are
+ * NULL and the tensor is not cast.  A cast tensor needs numel[i] % 16 == 0;
+ * at least one tensor must be cast (else MP_ERR_INVALID). */
+mp_status mp_fp8set_create(const mp_plan* plan, void* const* codes, void* const* scales,
+                           mp_fp8set** out);
+mp_status mp_fp8set_destroy(mp_fp8set* set);
+
+/* mp_adamw_step with the FP8 cast of the new weights fused into the same pass:
+ * everything mp_adamw_step writes, bit for bit, and for every cast tensor of
+ * `fp8` the codes and scales that mp_cast_fp8_blocks with block = 16 would
+ * write for the new fp32 masters.  The masters are cast while they are in
+ * registers, so the cast costs its 1.25 bytes/param of writes, not a second
+ * 4-byte read.  Same order rules as mp_adamw_step; on a skipped step
+ * (found_inf) nothing is written, the FP8 outputs included. */
+mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                            int32_t last_is_first, const mp_adamw_hparams* hp,
+                            const mp_fp8set* fp8, mp_stream stream);
 
 #ifdef __cplusplus
 }

@@ -16,8 +16,10 @@ Workloads (ids are stream labels):
   N(0, 1e-4) gradients with a 1e-3 fraction scaled by 100
 * 4  ``ragged-4096``  4096 tensors, 4092 log-uniform sizes + {64, 65, 2^24-1, 2^24}; bf16, k=4
 * 5  ``llama3-8B``    d=4096, 32 layers, GQA kv 1024, ffn 14336, vocab 128256 untied; bf16, k=4
-* 13, 14, 15: reduced versions of 3, 4 and 5 for element-by-element parity, and
-  16: a list of edge-case sizes around the kernels' tile boundaries.
+* 13, 14, 15: reduced versions of 3, 4 and 5 for element-by-element parity;
+  16, 17, 19: lists of edge-case sizes around the kernels' tile boundaries (bf16; fp16 with
+  a dynamic scale and an injected overflow; the same on sizes that are multiples of 16);
+  18: the fp16 run's scaler over 2003 steps on three small tensors.
 """
 import math
 
@@ -154,6 +156,13 @@ def make(name):
         return Workload(17, name, [("f%02d" % i, (n,)) for i, n in enumerate(sizes)], FP16, 2,
                         grad_kind=LOGUNIF_MIX, tail_prob=0.05, lo_exp=-30, hi_exp=-20,
                         scaler=dict(FP16_SCALER, interval=2), inject_step=2, steps=6)
+    if name == "edges-fp16-b16":
+        # the fp16 edge list's recipe, scaler and overflow on sizes that are mostly multiples of
+        # 16 around the tile boundaries (for the fused block-16 FP8 cast), plus three that are not
+        sizes = [16, 32, 48, 2032, 2048, 2064, 4112, 65536, 1, 9, 300007]
+        return Workload(19, name, [("b%02d" % i, (n,)) for i, n in enumerate(sizes)], FP16, 2,
+                        grad_kind=LOGUNIF_MIX, tail_prob=0.05, lo_exp=-30, hi_exp=-20,
+                        scaler=dict(FP16_SCALER, interval=2), inject_step=2, steps=5)
     if name == "gpt-124M-scaler":
         # the fp16 run's scaler, overflow and gradient recipe on a small tensor list, long enough
         # for the scale to grow back: 2000 clean steps after the overflow of step 3

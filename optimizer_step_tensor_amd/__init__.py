@@ -30,7 +30,7 @@ ENTRY_POINTS = [
     "mp_state_read", "mp_state_scale_ptr", "mp_accumulate", "mp_unscale_check_norm",
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
-    "mp_cast_fp8_blocks",
+    "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -112,6 +112,9 @@ def _bind(L):
         "mp_norm_partial": ([P, P, P, f32, i32, P, P], i32),
         "mp_norm_finish": ([P, P, P, f32, P], i32),
         "mp_cast_fp8_blocks": ([P, P, P, i64, i32, P], i32),
+        "mp_fp8set_create": ([P, PP, PP, PP], i32),
+        "mp_fp8set_destroy": ([P], i32),
+        "mp_adamw_step_fp8": ([P, P, P, f32, i32, ctypes.POINTER(AdamWHparams), P, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -290,6 +293,22 @@ def mp_norm_finish(plan, state, sumsq, max_norm, stream=None):
 def mp_cast_fp8_blocks(src, codes, scales, n, block=16, stream=None):
     _check(lib().mp_cast_fp8_blocks(ctypes.c_void_p(src), ctypes.c_void_p(codes),
                                     ctypes.c_void_p(scales), int(n), int(block), _stream(stream)))
+
+
+def mp_fp8set_create(plan, codes, scales):
+    """codes[i], scales[i]: tensors / device addresses, or None for a tensor that is not cast."""
+    out = ctypes.c_void_p()
+    _check(lib().mp_fp8set_create(plan, _ptrs(codes), _ptrs(scales), ctypes.byref(out)))
+    return out
+
+
+def mp_fp8set_destroy(fp8set):
+    _check(lib().mp_fp8set_destroy(fp8set))
+
+
+def mp_adamw_step_fp8(plan, state, last, w_last, last_is_first, hp, fp8set, stream=None):
+    _check(lib().mp_adamw_step_fp8(plan, state, last, float(w_last), int(bool(last_is_first)),
+                                   ctypes.byref(hp), fp8set, _stream(stream)))
 
 
 # --- convenience ---------------------------------------------------------------

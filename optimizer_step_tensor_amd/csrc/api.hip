@@ -12,6 +12,7 @@
 
 using mpk::Chunk;
 using mpk::DevState;
+using mpk::Fp8Out;
 using mpk::TensorDesc;
 
 struct mp_plan {
@@ -35,11 +36,17 @@ struct mp_plan {
     const mp_gradset* norm_last;
     float norm_w_last;
     int32_t norm_last_is_first;
+    std::vector<int64_t> numel;  // per tensor, for validating FP8 output sets
 };
 
 struct mp_gradset {
     const mp_plan* plan;
     uint16_t** d_ptrs;
+};
+
+struct mp_fp8set {
+    const mp_plan* plan;
+    Fp8Out* d_out;            // one entry per tensor of the plan
 };
 
 struct mp_state {
@@ -300,6 +307,7 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
     p->chunk_elems = ch;
     p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
     p->norm_grid = p->grid;
+    p->numel.assign(numel, numel + n_tensors);
     // every partial sum is written by its block before any kernel reads it
     const size_t partial_bytes = (static_cast<size_t>(p->norm_grid) + mpk::kNormStage2) * sizeof(double);
     if ((e = upload(&p->d_tensors, tensors)) != hipSuccess ||
@@ -384,6 +392,54 @@ mp_status mp_gradset_destroy(mp_gradset* set)
 {
     if (set == nullptr) return ok();
     (void)hipFree(set->d_ptrs);
+    delete set;
+    return ok();
+}
+
+mp_status mp_fp8set_create(const mp_plan* plan, void* const* codes, void* const* scales,
+                           mp_fp8set** out)
+{
+    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (plan == nullptr || codes == nullptr || scales == nullptr)
+        return fail(MP_ERR_INVALID, "plan, codes and scales are required");
+    std::vector<Fp8Out> outs(plan->n_tensors);
+    int32_t n_cast = 0;
+    for (int32_t i = 0; i < plan->n_tensors; ++i) {
+        if (codes[i] == nullptr && scales[i] == nullptr) {
+            outs[i] = Fp8Out{nullptr, nullptr};
+            continue;
+        }
+        if (codes[i] == nullptr || scales[i] == nullptr)
+            return fail(MP_ERR_INVALID, "tensor %d: codes and scales must both be set or both NULL", i);
+        if (plan->numel[i] % 16 != 0)
+            return fail(MP_ERR_INVALID, "tensor %d: numel %lld is not a multiple of 16", i,
+                        (long long)plan->numel[i]);
+        if (!aligned16(codes[i]) || (reinterpret_cast<uintptr_t>(scales[i]) & 3u) != 0)
+            return fail(MP_ERR_ALIGN, "tensor %d: codes must be 16-byte aligned, scales 4-byte aligned", i);
+        outs[i] = Fp8Out{static_cast<uint8_t*>(codes[i]), static_cast<float*>(scales[i])};
+        ++n_cast;
+    }
+    if (n_cast == 0) return fail(MP_ERR_INVALID, "no tensor has FP8 outputs");
+    mp_status st = check_device(plan->device, "the plan");
+    if (st != MP_OK) return st;
+    mp_fp8set* f = new (std::nothrow) mp_fp8set();
+    if (f == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+    f->plan = plan;
+    hipError_t e = upload(&f->d_out, outs);
+    if (e != hipSuccess) {
+        delete f;
+        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
+                                        : hip_fail(e, "fp8 set upload");
+    }
+    *out = f;
+    return ok();
+}
+
+mp_status mp_fp8set_destroy(mp_fp8set* set)
+{
+    if (set == nullptr) return ok();
+    (void)hipFree(set->d_out);
     delete set;
     return ok();
 }
@@ -600,8 +656,11 @@ mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, fl
     return ok();
 }
 
-mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
-                        int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
+namespace {
+
+mp_status adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                     int32_t last_is_first, const mp_adamw_hparams* hp, const Fp8Out* fp8,
+                     mp_stream stream)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     mp_status st = check_hparams(hp);
@@ -611,17 +670,34 @@ mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, 
     if (!plan->norm_pending || plan->norm_state != state || plan->norm_last != last ||
         (last != nullptr && (plan->norm_w_last != w_last ||
                              plan->norm_last_is_first != (last_is_first ? 1 : 0))))
-        return fail(MP_ERR_ORDER, "mp_adamw_step must follow mp_unscale_check_norm on the same "
+        return fail(MP_ERR_ORDER, "the AdamW step must follow mp_unscale_check_norm on the same "
                                   "plan and state, with the same last micro-batch arguments");
     st = check_devices(plan, state);
     if (st != MP_OK) return st;
     mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
     hipError_t e = mpk::launch_adamw(view(plan), plan->grid, last ? last->d_ptrs : nullptr, w_last,
-                                     grad_mode(last, last_is_first), plan->dtype, a, state->d,
+                                     grad_mode(last, last_is_first), plan->dtype, a, fp8, state->d,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "adamw launch");
     plan->norm_pending = false;
     return ok();
+}
+
+}  // namespace
+
+mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                        int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
+{
+    return adamw_step(plan, state, last, w_last, last_is_first, hp, nullptr, stream);
+}
+
+mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                            int32_t last_is_first, const mp_adamw_hparams* hp,
+                            const mp_fp8set* fp8, mp_stream stream)
+{
+    if (fp8 == nullptr) return fail(MP_ERR_INVALID, "fp8 set is NULL");
+    if (fp8->plan != plan) return fail(MP_ERR_INVALID, "fp8 set belongs to another plan");
+    return adamw_step(plan, state, last, w_last, last_is_first, hp, fp8->d_out, stream);
 }
 
 mp_status mp_scaler_update(mp_state* state, mp_stream stream)

@@ -96,6 +96,13 @@ struct AdamArgs {
     float lr, beta1, beta2, eps, weight_decay;
 };
 
+// FP8 (E4M3) outputs of one tensor for the fused AdamW pass: numel codes and
+// numel/16 block scales, or both NULL (the tensor is not cast).
+struct Fp8Out {
+    uint8_t* codes;
+    float* scales;
+};
+
 // How the gradient of one element is formed (see mp_unscale_check_norm).
 enum GradMode { kAccOnly = 0, kLastOnly = 1, kAccPlusLast = 2 };
 
@@ -109,7 +116,8 @@ hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* cons
                                const DevState* st, double* out, hipStream_t s);
 hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s);
 hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
-                        int mode, int dtype, const AdamArgs& a, DevState* st, hipStream_t s);
+                        int mode, int dtype, const AdamArgs& a, const Fp8Out* fp8, DevState* st,
+                        hipStream_t s);
 hipError_t launch_scaler(DevState* st, hipStream_t s);
 hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s);
 hipError_t launch_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n, int block,

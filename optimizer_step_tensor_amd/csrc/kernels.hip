@@ -379,12 +379,80 @@ __global__ void k_norm_apply(const double* __restrict__ sumsq, float max_norm,
 }
 
 // ---------------------------------------------------------------------------
-// AdamW on fp32 master/m/v and the RNE cast to the 16-bit weight.
+// Fine-grained FP8 ("Chapter 41 Training at Scale", section 41.5): blocks of
+// consecutive values; scale = max|x| / 448 (a zero block takes 1); each value
+// x / scale rounded to E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no
+// infinity: saturate at 448; NaN -> S.1111.111).
 // ---------------------------------------------------------------------------
-template <int DT, int MODE>
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7Fu;                  // NaN
+    if (a >= 0x43E80000u) return sign | 0x7Eu;                 // >= 464 (incl. inf): 448
+    if (a >= 0x3C800000u) {                                    // >= 2^-6: normal
+        // round the 23-bit mantissa to 3 bits, ties to even, then rebias 127 -> 7
+        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        return sign | ((r >> 20) - (120u << 3));
+    }
+    // subnormal: the nearest multiple of 2^-9 (ties to even); 8 * 2^-9 is the
+    // smallest normal, whose code is 8 as well
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | static_cast<uint32_t>(m);
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
+{
+    return e4m3_code(x.v[0] / scale) | (e4m3_code(x.v[1] / scale) << 8) |
+           (e4m3_code(x.v[2] / scale) << 16) | (e4m3_code(x.v[3] / scale) << 24);
+}
+
+// Scale of the 16-value block held by lanes 4q..4q+3 (4 consecutive values
+// each): the lanes' maxima combined with two butterfly shuffles.  Every lane
+// of the wave must call it.  A NaN never wins a comparison.
+__device__ __forceinline__ float block16_scale(const F4& x)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        const float a = __builtin_fabsf(x.v[k]);
+        amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1) {
+        const float o = __shfl_xor(amax, off, kWave);
+        amax = o > amax ? o : amax;
+    }
+    float scale = amax / 448.0f;
+    if (scale == 0.0f) scale = 1.0f;
+    return scale;
+}
+
+__device__ __forceinline__ void store_codes4(uint8_t* p, uint32_t packed)
+{
+    MPK_GLOBAL uint32_t* q = (MPK_GLOBAL uint32_t*)(p);
+    if (MPK_NT_STORES) __builtin_nontemporal_store(packed, q);
+    else *q = packed;
+}
+
+__device__ __forceinline__ void store_scale(float* p, float scale)
+{
+    MPK_GLOBAL float* q = (MPK_GLOBAL float*)(p);
+    if (MPK_NT_STORES) __builtin_nontemporal_store(scale, q);
+    else *q = scale;
+}
+
+// ---------------------------------------------------------------------------
+// AdamW on fp32 master/m/v and the RNE cast to the 16-bit weight.  With FP8,
+// the new weights of every tensor that has FP8 outputs are also cast in blocks
+// of 16 exactly as k_fp8_blocks16 casts them, in the same pass.
+// ---------------------------------------------------------------------------
+template <int DT, int MODE, bool FP8>
 __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
                                                   const uint16_t* const* __restrict__ last,
                                                   float w_last, AdamArgs a,
+                                                  const Fp8Out* __restrict__ fp8,
                                                   const DevState* __restrict__ st)
 {
     if (st->s.found_inf) return;                  // skipped step: write nothing
@@ -405,6 +473,17 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
         float* mm = td.m + ch.start;
         float* mv = td.v + ch.start;
         uint16_t* w16 = td.w16 + ch.start;
+        // a cast tensor has numel % 16 == 0, so with chunk starts on 2048 every
+        // group of 4 is wholly inside or wholly past its tensor's end
+        uint8_t* codes = nullptr;
+        float* scales = nullptr;
+        if (FP8) {
+            const Fp8Out o = fp8[ch.tensor];
+            if (o.codes != nullptr) {
+                codes = o.codes + ch.start;
+                scales = o.scales + ch.start / 16;
+            }
+        }
         for_each_pass(ch.len, [&](auto full, int base) {
             constexpr bool F = decltype(full)::value;
             int e[kGroupsPerLane], nv[kGroupsPerLane];
@@ -445,6 +524,13 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
                 store_f4<F>(mm + e[j], m[j], nv[j]);
                 store_f4<F>(mv + e[j], v[j], nv[j]);
                 store_h4<F>(w16 + e[j], out16, nv[j]);
+                if (FP8 && codes != nullptr) {          // uniform over the block
+                    const float scale = block16_scale(wv[j]);
+                    if (F || nv[j] >= kGroup) {
+                        store_codes4(codes + e[j], pack_e4m3(wv[j], scale));
+                        if ((threadIdx.x & 3) == 0) store_scale(scales + e[j] / 16, scale);
+                    }
+                }
             }
         });
     }
@@ -505,36 +591,6 @@ __global__ __launch_bounds__(kBlock) void k_widen_16(const uint16_t* __restrict_
         dst[i] = widen16<DT>(src[i]);
 }
 
-// ---------------------------------------------------------------------------
-// Fine-grained FP8 ("Chapter 41 Training at Scale", section 41.5): one lane
-// per block of values; scale = max|x| / 448 (a zero block takes 1); each
-// value x / scale rounded to E4M3 (4 exponent bits, bias 7, 3 mantissa bits,
-// no infinity: saturate at 448; NaN -> S.1111.111).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_code(float v)
-{
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return sign | 0x7Fu;                  // NaN
-    if (a >= 0x43E80000u) return sign | 0x7Eu;                 // >= 464 (incl. inf): 448
-    if (a >= 0x3C800000u) {                                    // >= 2^-6: normal
-        // round the 23-bit mantissa to 3 bits, ties to even, then rebias 127 -> 7
-        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        return sign | ((r >> 20) - (120u << 3));
-    }
-    // subnormal: the nearest multiple of 2^-9 (ties to even); 8 * 2^-9 is the
-    // smallest normal, whose code is 8 as well
-    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
-    return sign | static_cast<uint32_t>(m);
-}
-
-__device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
-{
-    return e4m3_code(x.v[0] / scale) | (e4m3_code(x.v[1] / scale) << 8) |
-           (e4m3_code(x.v[2] / scale) << 16) | (e4m3_code(x.v[3] / scale) << 24);
-}
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Block of 16 (the listing's default): a wave covers 1024 consecutive values,
@@ -564,19 +620,7 @@ __global__ __launch_bounds__(kBlock) void k_fp8_blocks16(const float* __restrict
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t e = base + j * kSlab + lane * kGroup;
-            float amax = 0.0f;
-#pragma unroll
-            for (int k = 0; k < kGroup; ++k) {
-                const float a = __builtin_fabsf(v[j].v[k]);
-                amax = a > amax ? a : amax;                        // a NaN never wins
-            }
-#pragma unroll
-            for (int off = 1; off < 4; off <<= 1) {
-                const float o = __shfl_xor(amax, off, kWave);
-                amax = o > amax ? o : amax;
-            }
-            float scale = amax / 448.0f;
-            if (scale == 0.0f) scale = 1.0f;
+            const float scale = block16_scale(v[j]);
             if (live[j]) {
                 *(MPK_GLOBAL uint32_t*)(codes + e) = pack_e4m3(v[j], scale);
                 if ((lane & 3) == 0) scales[e / 16] = scale;
@@ -636,9 +680,10 @@ void launch_norm_t(const PlanView& p, int grid, const uint16_t* const* last, flo
 
 template <int DT, int MODE>
 void launch_adamw_t(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
-                    const AdamArgs& a, DevState* st, hipStream_t s)
+                    const AdamArgs& a, const Fp8Out* fp8, DevState* st, hipStream_t s)
 {
-    k_adamw<DT, MODE><<<grid, kBlock, 0, s>>>(p, last, w_last, a, st);
+    if (fp8 != nullptr) k_adamw<DT, MODE, true><<<grid, kBlock, 0, s>>>(p, last, w_last, a, fp8, st);
+    else                k_adamw<DT, MODE, false><<<grid, kBlock, 0, s>>>(p, last, w_last, a, fp8, st);
 }
 
 }  // namespace
@@ -706,16 +751,17 @@ hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, 
 }
 
 hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
-                        int mode, int dtype, const AdamArgs& a, DevState* st, hipStream_t s)
+                        int mode, int dtype, const AdamArgs& a, const Fp8Out* fp8, DevState* st,
+                        hipStream_t s)
 {
     if (dtype == MP_BF16) {
-        if (mode == kAccOnly)       launch_adamw_t<MP_BF16, kAccOnly>(p, grid, last, w_last, a, st, s);
-        else if (mode == kLastOnly) launch_adamw_t<MP_BF16, kLastOnly>(p, grid, last, w_last, a, st, s);
-        else                        launch_adamw_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, a, st, s);
+        if (mode == kAccOnly)       launch_adamw_t<MP_BF16, kAccOnly>(p, grid, last, w_last, a, fp8, st, s);
+        else if (mode == kLastOnly) launch_adamw_t<MP_BF16, kLastOnly>(p, grid, last, w_last, a, fp8, st, s);
+        else                        launch_adamw_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, a, fp8, st, s);
     } else {
-        if (mode == kAccOnly)       launch_adamw_t<MP_FP16, kAccOnly>(p, grid, last, w_last, a, st, s);
-        else if (mode == kLastOnly) launch_adamw_t<MP_FP16, kLastOnly>(p, grid, last, w_last, a, st, s);
-        else                        launch_adamw_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, a, st, s);
+        if (mode == kAccOnly)       launch_adamw_t<MP_FP16, kAccOnly>(p, grid, last, w_last, a, fp8, st, s);
+        else if (mode == kLastOnly) launch_adamw_t<MP_FP16, kLastOnly>(p, grid, last, w_last, a, fp8, st, s);
+        else                        launch_adamw_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, a, fp8, st, s);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

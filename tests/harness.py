@@ -83,6 +83,7 @@ class DeviceRun:
         self.state = mp.mp_state_create(cfg)
         self.hp = mp.adamw_hparams(**w.hp)
         self.step_no = 0
+        self.fp8set = None                 # set: steps use the fused AdamW + FP8 entry point
 
     def stats(self):
         return self.mp.read_stats(self.state)
@@ -112,7 +113,11 @@ class DeviceRun:
                         if snapshot and self.model.acc is not None else None)
         last, lif = self.gsets[w.k - 1], w.k == 1
         mp.mp_unscale_check_norm(self.model.plan, self.state, last, weights[-1], lif, w.max_norm)
-        mp.mp_adamw_step(self.model.plan, self.state, last, weights[-1], lif, self.hp)
+        if self.fp8set is None:
+            mp.mp_adamw_step(self.model.plan, self.state, last, weights[-1], lif, self.hp)
+        else:
+            mp.mp_adamw_step_fp8(self.model.plan, self.state, last, weights[-1], lif, self.hp,
+                                 self.fp8set)
         mp.mp_scaler_update(self.state)
         return acc_snapshot
 

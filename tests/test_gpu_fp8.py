@@ -100,3 +100,89 @@ def test_fp8_argument_errors(mp):
         with pytest.raises(mp.MpError) as e:
             mp.mp_cast_fp8_blocks(x.data_ptr(), c.data_ptr(), s.data_ptr(), n, block)
         assert e.value.status == mp.MP_ERR_INVALID
+
+
+@pytest.mark.parametrize("name", ["edges", "edges-fp16-b16", "llama3-8B-small"])
+def test_adamw_fp8_fused_matches_the_oracle(mp, name):
+    """mp_adamw_step_fp8: the step equals the oracle exactly as mp_adamw_step does, and every cast
+    tensor's codes and scales equal the oracle's block-16 cast of the new masters, bit for bit.
+    Tensors whose numel is not a multiple of 16 are left uncast; on a skipped step (the fp16 list
+    injects an inf) nothing is written."""
+    import torch
+    from inputs import configs
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make(name)
+    say("workload %s: %d tensors, k=%d, %d steps" % (name, len(w.tensors), w.k, w.steps))
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    cast = [t for t, n in enumerate(w.numels) if n % 16 == 0]
+    assert cast
+    codes = [None] * len(w.numels)
+    scales = [None] * len(w.numels)
+    for t in cast:
+        codes[t] = torch.full((w.numels[t],), 0x5A, dtype=torch.uint8, device="cuda")
+        scales[t] = torch.full((w.numels[t] // 16,), -1.0, dtype=torch.float32, device="cuda")
+    dev.fp8set = mp.mp_fp8set_create(dev.model.plan, codes, scales)
+    try:
+        prev = {t: (codes[t].cpu().numpy(), scales[t].cpu().numpy()) for t in cast}
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            rep = compare_step(dev, orc, w, s)
+            masters = dev.host("master")
+            got = {t: (codes[t].cpu().numpy(), scales[t].cpu().numpy()) for t in cast}
+            for t in cast:
+                if orc.st.found_inf:
+                    want = prev[t]
+                else:
+                    want = oracle.fp8_block_cast(masters[t], 16)
+                    # the device masters are the oracle's whenever the norms agree bit for bit
+                    if rep["same_norm_bits"]:
+                        assert np.array_equal(masters[t].view(np.uint32),
+                                              orc.st.masters[t].view(np.uint32))
+                assert np.array_equal(got[t][0], want[0]), (s, t)
+                assert np.array_equal(got[t][1].view(np.uint32), want[1].view(np.uint32)), (s, t)
+            prev = got
+            say("  step", s, "found_inf", int(orc.st.found_inf), "cast tensors", len(cast))
+    finally:
+        mp.mp_fp8set_destroy(dev.fp8set)
+        dev.close()
+
+
+def test_fp8set_argument_errors(mp):
+    import torch
+    from inputs import configs
+    from harness import DeviceRun
+    w = configs.make("edges")
+    dev = DeviceRun(w)
+    try:
+        n = len(w.numels)
+        bad = w.numels.index(7)                       # not a multiple of 16
+        c = [None] * n
+        sc = [None] * n
+        with pytest.raises(mp.MpError) as e:          # nothing to cast
+            mp.mp_fp8set_create(dev.model.plan, c, sc)
+        assert e.value.status == mp.MP_ERR_INVALID
+        c[bad] = torch.empty(16, dtype=torch.uint8, device="cuda")
+        sc[bad] = torch.empty(1, dtype=torch.float32, device="cuda")
+        with pytest.raises(mp.MpError) as e:
+            mp.mp_fp8set_create(dev.model.plan, c, sc)
+        assert e.value.status == mp.MP_ERR_INVALID
+        good = w.numels.index(256)
+        c = [None] * n
+        sc = [None] * n
+        c[good] = torch.empty(256, dtype=torch.uint8, device="cuda")
+        with pytest.raises(mp.MpError) as e:          # scales missing
+            mp.mp_fp8set_create(dev.model.plan, c, sc)
+        assert e.value.status == mp.MP_ERR_INVALID
+        sc[good] = torch.empty(16, dtype=torch.float32, device="cuda")
+        fs = mp.mp_fp8set_create(dev.model.plan, c, sc)
+        try:
+            with pytest.raises(mp.MpError) as e:      # the AdamW order rules hold
+                mp.mp_adamw_step_fp8(dev.model.plan, dev.state, None, 1.0, 0, dev.hp, fs)
+            assert e.value.status == mp.MP_ERR_ORDER
+        finally:
+            mp.mp_fp8set_destroy(fs)
+    finally:
+        dev.close()
