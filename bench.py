@@ -137,9 +137,56 @@ def time_launches(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def run_extras(mp, torch, w, model, g16, hp, weights, stream):
+def time_fused_fp8(mp, torch, w, model, sets, state, hp, weights, stream, reps=3):
+    """AdamW with the block-16 FP8 cast of every tensor whose size allows it, fused, and the
+    plain AdamW pass, each timed with HIP events around its own launch."""
+    k = w.k
+    offs, total = [], 0
+    for n in w.numels:
+        offs.append(total)
+        total += (n + 15) // 16 * 16
+    codes = torch.empty(total, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(total // 16, dtype=torch.float32, device="cuda")
+    cv = [codes[o:o + n] if n % 16 == 0 else None for o, n in zip(offs, w.numels)]
+    sv = [scales[o // 16:o // 16 + n // 16] if n % 16 == 0 else None
+          for o, n in zip(offs, w.numels)]
+    n_cast = sum(n for n in w.numels if n % 16 == 0)
+    fs = mp.mp_fp8set_create(model.plan, cv, sv)
+    lif = k == 1
+    times = {"fused": [], "plain": []}
+    try:
+        for _ in range(reps + 1):
+            for kind in ("fused", "plain"):
+                mp.mp_unscale_check_norm(model.plan, state, sets[-1], weights[-1], lif, w.max_norm,
+                                         stream)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                if kind == "fused":
+                    mp.mp_adamw_step_fp8(model.plan, state, sets[-1], weights[-1], lif, hp, fs,
+                                         stream)
+                else:
+                    mp.mp_adamw_step(model.plan, state, sets[-1], weights[-1], lif, hp, stream)
+                e1.record(stream)
+                mp.mp_scaler_update(state, stream)
+                times[kind].append((e0, e1))
+        torch.cuda.synchronize()
+    finally:
+        mp.mp_fp8set_destroy(fs)
+    ms = {kind: sum(a.elapsed_time(b) for a, b in v[1:]) / reps for kind, v in times.items()}
+    adam_bpp = bytes_per_param(k)["adamw"]
+    fused_bytes = adam_bpp * w.total + 1.25 * n_cast
+    return {"elements_cast": n_cast, "ms": ms["fused"], "plain_adamw_ms": ms["plain"],
+            "extra_ms": ms["fused"] - ms["plain"], "bytes": fused_bytes,
+            "GBps": fused_bytes / ms["fused"] / 1e6,
+            "frac": fused_bytes / ms["fused"] / 1e6 / HBM_PEAK_GBPS}
+
+
+def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
     """The rows after the hot path, on the same resident buffers:
     - the fine-grained FP8 cast (block 16) of every fp32 master;
+    - the same cast fused into the AdamW pass (mp_adamw_step_fp8), against the plain AdamW pass
+      timed the same way in alternation;
     - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
       multiples of 8 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
     out = {}
@@ -166,6 +213,8 @@ def run_extras(mp, torch, w, model, g16, hp, weights, stream):
     gbps = n_cast * (4 + 1 + 4 / 16) / ms / 1e6
     out["fp8_block_cast"] = {"block": 16, "elements": n_cast, "ms": ms,
                              "bytes_per_element": 5.25, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+    del codes, scales
+    out["adamw_fp8_fused"] = time_fused_fp8(mp, torch, w, model, sets, state, hp, weights, stream)
     ranks, r = 8, 0
     numel, ptrs = [], {"acc": [], "master": [], "m": [], "v": [], "w16": []}
     gp = [[] for _ in range(k)]
@@ -387,7 +436,8 @@ def main():
         % (ms_per_step, step_bytes / ms_per_step / 1e6, step_bytes / ms_per_step / 1e6 /
            HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
 
-    extras = None if args.no_extras else run_extras(mp, torch, w, model, g16, hp, weights, stream)
+    extras = None if args.no_extras else run_extras(mp, torch, w, model, g16, sets, state, hp,
+                                                    weights, stream)
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,
