@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -404,16 +405,16 @@ def main():
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(args.steps):
+        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        bounds[0].record(stream)
+        for i in range(args.steps):
             one_step(record)
-        g1.record(stream)
+            bounds[i + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        gpu_ms = g0.elapsed_time(g1)
+        gpu_ms = bounds[0].elapsed_time(bounds[-1])
         ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
+        step_ms = [a.elapsed_time(b) for a, b in zip(bounds, bounds[1:])]
     stats = mp.read_stats(state)
     log("stats after timing:", stats)
 
@@ -464,6 +465,8 @@ def main():
                    "step_GBps": step_bytes / ms_per_step / 1e6,
                    "step_hbm_frac": step_bytes / ms_per_step / 1e6 / HBM_PEAK_GBPS,
                    "kernel_ms": kernel_ms,
+                   "step_ms_median": statistics.median(step_ms),
+                   "step_ms_min": min(step_ms), "step_ms_max": max(step_ms),
                    "chunk_elems": info["chunk_elems"], "n_chunks": info["n_chunks"]},
         "roofline": {"bound": "hbm", "kernel": "k_adamw (AdamW + RNE cast, last micro-batch "
                                                 "folded in)",
