@@ -170,9 +170,22 @@ mp_status mp_chunk_layout(int32_t n_tensors, const int64_t* numel, int32_t n_cus
 
 /* One micro-batch's 16-bit gradients: g16[i] points at numel[i] elements of
  * the plan's 16-bit format, in the caller's device memory.  The pointer list
- * is uploaded once (synchronously), so a gradset can be reused every step. */
+ * is uploaded once (synchronously), so a gradset can be reused every step.
+ * Destroy a gradset only after the stream work that uses it has finished. */
 mp_status mp_gradset_create(const mp_plan* plan, void* const* g16, mp_gradset** out);
 mp_status mp_gradset_destroy(mp_gradset* set);
+
+/* Point an existing gradset at other gradient buffers (same plan, same rules
+ * as mp_gradset_create), for callers whose gradient tensors move between
+ * steps (e.g. freed and reallocated by the framework).  Allocates nothing: the
+ * new pointer list is written into one of 4 pinned host slots owned by the
+ * gradset and copied to the device on `stream`, so work enqueued on `stream`
+ * after this call sees the new buffers and work enqueued before it the old
+ * ones.  Before rewriting a slot the call waits until the copy that last read
+ * it has run, so the host can run at most 4 updates ahead of the device.
+ * Refused (MP_ERR_INVALID) while `stream` is being captured into a graph: a
+ * replay would copy whatever the slot holds at replay time. */
+mp_status mp_gradset_update(mp_gradset* set, void* const* g16, mp_stream stream);
 
 /* Device state: S = init_scale, no good steps, t = 0, beta powers 1. */
 mp_status mp_state_create(const mp_scaler_cfg* cfg, mp_state** out);

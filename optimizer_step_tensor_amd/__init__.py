@@ -31,6 +31,7 @@ ENTRY_POINTS = [
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
+    "mp_gradset_update",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -115,6 +116,7 @@ def _bind(L):
         "mp_fp8set_create": ([P, PP, PP, PP], i32),
         "mp_fp8set_destroy": ([P], i32),
         "mp_adamw_step_fp8": ([P, P, P, f32, i32, ctypes.POINTER(AdamWHparams), P, P], i32),
+        "mp_gradset_update": ([P, PP, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -217,6 +219,10 @@ def mp_gradset_create(plan, g16):
     out = ctypes.c_void_p()
     _check(lib().mp_gradset_create(plan, _ptrs(g16), ctypes.byref(out)))
     return out
+
+
+def mp_gradset_update(gradset, g16, stream=None):
+    _check(lib().mp_gradset_update(gradset, _ptrs(g16), _stream(stream)))
 
 
 def mp_gradset_destroy(gradset):

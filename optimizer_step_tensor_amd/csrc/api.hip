@@ -39,9 +39,17 @@ struct mp_plan {
     std::vector<int64_t> numel;  // per tensor, for validating FP8 output sets
 };
 
+constexpr int kGradsetSlots = 4;   // pinned staging slots of mp_gradset_update
+
 struct mp_gradset {
     const mp_plan* plan;
     uint16_t** d_ptrs;
+    // mp_gradset_update stages each new table in one of these pinned host
+    // slots, round robin; a slot is rewritten only after the copy that last
+    // read it has run (its event)
+    uint16_t** h_slots[kGradsetSlots];
+    hipEvent_t copied[kGradsetSlots];
+    int next_slot;
 };
 
 struct mp_fp8set {
@@ -364,35 +372,90 @@ mp_status mp_chunk_layout(int32_t n_tensors, const int64_t* numel, int32_t n_cus
     return ok();
 }
 
-mp_status mp_gradset_create(const mp_plan* plan, void* const* g16, mp_gradset** out)
+namespace {
+
+mp_status check_grad_ptrs(const mp_plan* plan, void* const* g16, std::vector<uint16_t*>& ptrs)
 {
-    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
-    *out = nullptr;
-    if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and g16 are required");
-    std::vector<uint16_t*> ptrs(plan->n_tensors);
+    ptrs.resize(plan->n_tensors);
     for (int32_t i = 0; i < plan->n_tensors; ++i) {
         if (g16[i] == nullptr) return fail(MP_ERR_INVALID, "gradient %d is NULL", i);
         if (!aligned16(g16[i])) return fail(MP_ERR_ALIGN, "gradient %d not 16-byte aligned", i);
         ptrs[i] = static_cast<uint16_t*>(g16[i]);
     }
+    return MP_OK;
+}
+
+void free_gradset(mp_gradset* g)
+{
+    for (int i = 0; i < kGradsetSlots; ++i) {
+        if (g->copied[i] != nullptr) {
+            (void)hipEventSynchronize(g->copied[i]);   // no pending copy reads the slot
+            (void)hipEventDestroy(g->copied[i]);
+        }
+        if (g->h_slots[i] != nullptr) (void)hipHostFree(g->h_slots[i]);
+    }
+    (void)hipFree(g->d_ptrs);
+    delete g;
+}
+
+}  // namespace
+
+mp_status mp_gradset_create(const mp_plan* plan, void* const* g16, mp_gradset** out)
+{
+    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and g16 are required");
+    std::vector<uint16_t*> ptrs;
+    mp_status st = check_grad_ptrs(plan, g16, ptrs);
+    if (st != MP_OK) return st;
     mp_gradset* g = new (std::nothrow) mp_gradset();
     if (g == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
     g->plan = plan;
     hipError_t e = upload(&g->d_ptrs, ptrs);
+    const size_t slot_bytes = ptrs.size() * sizeof(uint16_t*);
+    for (int i = 0; i < kGradsetSlots && e == hipSuccess; ++i) {
+        e = hipHostMalloc(reinterpret_cast<void**>(&g->h_slots[i]), slot_bytes, hipHostMallocDefault);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&g->copied[i], hipEventDisableTiming);
+    }
     if (e != hipSuccess) {
-        delete g;
-        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
+        free_gradset(g);
+        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "allocation failed")
                                         : hip_fail(e, "gradset upload");
     }
     *out = g;
     return ok();
 }
 
+mp_status mp_gradset_update(mp_gradset* set, void* const* g16, mp_stream stream)
+{
+    if (set == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "gradset and g16 are required");
+    std::vector<uint16_t*> ptrs;
+    mp_status st = check_grad_ptrs(set->plan, g16, ptrs);
+    if (st == MP_OK) st = check_device(set->plan->device, "the gradset's plan");
+    if (st != MP_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(MP_ERR_INVALID, "mp_gradset_update cannot be captured in a graph: a replay "
+                                    "would copy whatever the staging slot holds then");
+    const int slot = set->next_slot;
+    e = hipEventSynchronize(set->copied[slot]);     // the copy that last read this slot has run
+    if (e != hipSuccess) return hip_fail(e, "gradset slot wait");
+    std::memcpy(set->h_slots[slot], ptrs.data(), ptrs.size() * sizeof(uint16_t*));
+    e = hipMemcpyAsync(set->d_ptrs, set->h_slots[slot], ptrs.size() * sizeof(uint16_t*),
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipEventRecord(set->copied[slot], s);
+    if (e != hipSuccess) return hip_fail(e, "gradset update");
+    set->next_slot = (slot + 1) % kGradsetSlots;
+    return ok();
+}
+
 mp_status mp_gradset_destroy(mp_gradset* set)
 {
     if (set == nullptr) return ok();
-    (void)hipFree(set->d_ptrs);
-    delete set;
+    free_gradset(set);
     return ok();
 }
 
