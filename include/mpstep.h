@@ -291,6 +291,15 @@ mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, 
  * mp_state_import leaves no measurement pending. */
 mp_status mp_scaler_update(mp_state* state, mp_stream stream);
 
+/* The whole update after the last micro-batch in one call: mp_unscale_check_norm,
+ * mp_adamw_step and mp_scaler_update with the same arguments, enqueued in that
+ * order on `stream` -- the scaler's step of "Mixed precision ...", section 4
+ * "The interface" (check, unscale, clip, optimizer step, update S).  Every
+ * structural check of the three calls is made before anything is enqueued. */
+mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                         int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
+                         mp_stream stream);
+
 /* Elementwise casts with the step's conversions: dst = round-to-nearest-even
  * of src into the 16-bit format (as in mp_adamw_step), and dst = exact fp32
  * value of a 16-bit pattern (as in mp_accumulate).  Useful to initialise the

@@ -31,7 +31,7 @@ ENTRY_POINTS = [
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
-    "mp_gradset_update",
+    "mp_gradset_update", "mp_update_step",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -117,6 +117,7 @@ def _bind(L):
         "mp_fp8set_destroy": ([P], i32),
         "mp_adamw_step_fp8": ([P, P, P, f32, i32, ctypes.POINTER(AdamWHparams), P, P], i32),
         "mp_gradset_update": ([P, PP, P], i32),
+        "mp_update_step": ([P, P, P, f32, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -262,6 +263,11 @@ def mp_unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, st
 def mp_adamw_step(plan, state, last, w_last, last_is_first, hp, stream=None):
     _check(lib().mp_adamw_step(plan, state, last, float(w_last), int(bool(last_is_first)),
                                ctypes.byref(hp), _stream(stream)))
+
+
+def mp_update_step(plan, state, last, w_last, last_is_first, max_norm, hp, stream=None):
+    _check(lib().mp_update_step(plan, state, last, float(w_last), int(bool(last_is_first)),
+                                float(max_norm), ctypes.byref(hp), _stream(stream)))
 
 
 def mp_scaler_update(state, stream=None):

@@ -763,6 +763,24 @@ mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* la
     return adamw_step(plan, state, last, w_last, last_is_first, hp, fp8->d_out, stream);
 }
 
+mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                         int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
+                         mp_stream stream)
+{
+    // every structural check first, so that an error enqueues nothing
+    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
+    mp_status st = check_hparams(hp);
+    if (st == MP_OK) st = check_last(plan, last, w_last, last_is_first);
+    if (st == MP_OK && (std::isnan(max_norm) || std::isinf(max_norm)))
+        st = fail(MP_ERR_INVALID, "max_norm must be finite");
+    if (st == MP_OK) st = check_devices(plan, state);
+    if (st != MP_OK) return st;
+    st = mp_unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream);
+    if (st == MP_OK) st = adamw_step(plan, state, last, w_last, last_is_first, hp, nullptr, stream);
+    if (st == MP_OK) st = mp_scaler_update(state, stream);
+    return st;
+}
+
 mp_status mp_scaler_update(mp_state* state, mp_stream stream)
 {
     if (state == nullptr) return fail(MP_ERR_INVALID, "state is NULL");

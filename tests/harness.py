@@ -84,6 +84,7 @@ class DeviceRun:
         self.hp = mp.adamw_hparams(**w.hp)
         self.step_no = 0
         self.fp8set = None                 # set: steps use the fused AdamW + FP8 entry point
+        self.one_call = False              # True: steps use mp_update_step
 
     def stats(self):
         return self.mp.read_stats(self.state)
@@ -112,6 +113,10 @@ class DeviceRun:
         acc_snapshot = ([a.cpu().numpy() for a in self.model.acc]
                         if snapshot and self.model.acc is not None else None)
         last, lif = self.gsets[w.k - 1], w.k == 1
+        if self.one_call:
+            mp.mp_update_step(self.model.plan, self.state, last, weights[-1], lif, w.max_norm,
+                              self.hp)
+            return acc_snapshot
         mp.mp_unscale_check_norm(self.model.plan, self.state, last, weights[-1], lif, w.max_norm)
         if self.fp8set is None:
             mp.mp_adamw_step(self.model.plan, self.state, last, weights[-1], lif, self.hp)

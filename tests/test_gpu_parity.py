@@ -125,6 +125,32 @@ def test_workload_parity(mp, name):
         dev.close()
 
 
+@pytest.mark.parametrize("name", ["edges-fp16", "llama-10.5M"])
+def test_update_step_in_one_call(mp, name):
+    """mp_update_step (unscale/check/norm, AdamW, scaler in one call) equals the oracle as the
+    three separate calls do, through an overflow and a change of S on the fp16 list."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make(name)
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    dev.one_call = True
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            say("  step", s, compare_step(dev, orc, w, s))
+        with pytest.raises(mp.MpError) as e:            # bad hyper-parameters: nothing enqueued
+            mp.mp_update_step(dev.model.plan, dev.state, dev.gsets[-1], 0.5, w.k == 1, 1.0,
+                              mp.adamw_hparams(eps=0.0))
+        assert e.value.status == mp.MP_ERR_INVALID
+        with pytest.raises(mp.MpError) as e:            # so no measurement is pending either
+            mp.mp_scaler_update(dev.state)
+        assert e.value.status == mp.MP_ERR_ORDER
+    finally:
+        dev.close()
+
+
 def test_norm_is_deterministic(mp):
     """The same inputs give the same sum of squares, bit for bit, on every run."""
     from harness import DeviceRun

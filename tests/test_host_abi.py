@@ -150,6 +150,7 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_adamw_step_fp8(None, None, None, 1.0, 0, None, None, None) == mp.MP_ERR_INVALID
     assert L.mp_fp8set_destroy(None) == mp.MP_OK
     assert L.mp_gradset_update(None, None, None) == mp.MP_ERR_INVALID
+    assert L.mp_update_step(None, None, None, 1.0, 0, 1.0, None, None) == mp.MP_ERR_INVALID
     assert (L.mp_norm_partial(fake_state, fake_state, None, 1.0, 0, ctypes.c_void_p(0x10001), None)
             == mp.MP_ERR_INVALID)
 
