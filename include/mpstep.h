@@ -323,9 +323,9 @@ mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dty
 mp_status mp_cast_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n,
                              int32_t block, mp_stream stream);
 
-/* FP8 outputs of selected tensors of a plan, for mp_adamw_step_fp8 ("Chapter
- * 41 Training at Scale", section 41.5: selected tensors stored or
- * communicated in FP8 with one scale per block).  For tensor i either both
+/* FP8 outputs for chosen tensors of a plan, for mp_adamw_step_fp8 ("Chapter
+ * 41 Training at Scale", section 41.5: FP8 copies kept for storage or
+ * transfer, each block of values with its own scale).  For tensor i either both
  * codes[i] (numel[i] bytes, 16-byte aligned) and scales[i] (numel[i]/16
  * floats, 4-byte aligned) are device pointers the caller owns, or both are
  * NULL and the tensor is not cast.  A cast tensor needs numel[i] % 16 == 0;
