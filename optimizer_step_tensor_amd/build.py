@@ -28,5 +28,21 @@ def build(out=LIB, extra=()):
     return out
 
 
+EXAMPLE_SRC = os.path.join(HERE, "examples", "c_api_step.cpp")
+EXAMPLE = os.path.join(HERE, "examples", "c_api_step")
+
+
+def build_example():
+    """The C example that drives the library with plain HIP allocations (host code only)."""
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wextra",
+           "-I", os.path.join(ROOT, "include"), "-o", EXAMPLE + ".tmp", EXAMPLE_SRC,
+           "-L", HERE, "-lmpstep", "-Wl,-rpath,$ORIGIN/.."]
+    subprocess.run(cmd, check=True)
+    os.replace(EXAMPLE + ".tmp", EXAMPLE)
+    return EXAMPLE
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_example())

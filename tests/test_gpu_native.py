@@ -1,0 +1,19 @@
+"""The C ABI without PyTorch (needs a GPU): optimizer_step_tensor_amd/examples/c_api_step,
+a plain HIP program built by __graft_entry__.build(), runs one update on hipMalloc'd buffers
+and checks it against closed forms (exact sum of squares, first AdamW step)."""
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EXAMPLE = os.path.join(ROOT, "optimizer_step_tensor_amd", "examples", "c_api_step")
+
+
+def test_c_example_runs_a_step():
+    assert os.path.exists(EXAMPLE), "the C example is not built; run __graft_entry__.build()"
+    r = subprocess.run([EXAMPLE], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0 and " ok " in r.stdout
