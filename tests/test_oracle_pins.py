@@ -536,6 +536,56 @@ def test_adamw_constant_gradient_trajectory():
     assert st.v[0][0] >= 0
 
 
+def _bf16_values(xs):
+    """The values as bf16 numbers (what the oracle sees after the 16-bit cast)."""
+    return [float(y) for y in oracle.widen16(oracle.rd16(np.asarray(xs, np.float32), BF16), BF16)]
+
+
+def test_adamw_moments_track_exact_moving_averages():
+    """lr = 0 freezes the weights, so only the moment recursion acts ('Your weights fit on one
+    device...': m and v are running averages of g and g^2 with decay beta).  Over 50 steps of
+    gradients that vary in sign and size, m and v stay within a rigorous fp32 rounding bound of
+    the exact averages m_t = b1 m_(t-1) + (1-b1) g_t and v_t = b2 v_(t-1) + (1-b2) g_t^2 (b the
+    fp32 betas, 1-b exact by Sterbenz), and the clock holds t = 50 and b^50 to binary64 accuracy."""
+    rng = np.random.default_rng(5)
+    gs = _bf16_values(rng.normal(0, 1, 50) * np.exp(rng.uniform(-6, 2, 50)))
+    st = _adam_run(gs, w0=0.5, lr=0.0)
+    assert st.masters[0][0] == np.float32(0.5)
+    u = 2.0 ** -24
+    for beta, got, sq in ((float(np.float32(0.9)), st.m[0][0], False),
+                          (float(np.float32(0.95)), st.v[0][0], True)):
+        exact, bound = 0.0, 0.0
+        for g in gs:
+            term = (1 - beta) * (g * g if sq else g)    # g*g is exact: bf16 has 8 bits
+            prev = exact
+            exact = beta * prev + term
+            # three roundings per step (product, product, sum), plus the carried error
+            bound = beta * bound + u * (abs(beta * prev) + abs(term) + abs(exact)) + 1e-45
+        assert abs(float(got) - exact) <= bound, (got, exact, bound)
+    assert st.clock.t == 50
+    for p, beta in ((st.clock.p1, float(np.float32(0.9))), (st.clock.p2, float(np.float32(0.95)))):
+        assert abs(p - beta ** 50) <= 1e-13 * beta ** 50
+
+
+def test_adamw_zero_betas_trajectory_with_varying_gradients():
+    """With b1 = b2 = 0 the moments are the current gradient and its square and both bias
+    corrections are 1, so every step is w <- w - lr (g/(|g| + eps) + lambda w) (decoupled decay,
+    'Accumulate gradients and recompute activations').  Thirty steps of gradients that change
+    sign and size, including a zero, follow that recursion to within a few fp32 roundings a
+    step."""
+    rng = np.random.default_rng(6)
+    raw = rng.normal(0, 1, 30) * np.exp(rng.uniform(-8, 3, 30))
+    raw[7] = 0.0
+    gs = _bf16_values(raw)
+    lr, wd, eps, w = 1e-2, 0.1, 1e-8, 0.75
+    st = _adam_run(gs, w0=w, lr=lr, b1=0.0, b2=0.0, eps=eps, wd=wd)
+    for g in gs:
+        u = g / (abs(g) + eps)
+        w = w - lr * (u + wd * w)
+    assert abs(st.masters[0][0] - w) <= 6 * len(gs) * ulp32(w)
+    assert st.m[0][0] == np.float32(gs[-1]) and st.v[0][0] == np.float32(gs[-1] ** 2)
+
+
 def test_master_absorbs_sub_spacing_update():
     """Section 2 'Why the weights stay float32': a weight of 1 updated by 1e-3 rounds back to 1 in
     bf16, but the fp32 master keeps the change; ten such updates move the bf16 copy."""
