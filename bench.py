@@ -75,13 +75,14 @@ def cpu_baseline(w, seconds_hint=20.0):
     grads = [[inputs.gen_host_u16(c, w.grad_recipe(1, i, t), w.dtype, off)
               for t, off, c in pieces] for i in range(w.k)]
     weights = oracle.token_weights(w.token_counts(1))
-    t0 = time.perf_counter()
+    t0, c0 = time.perf_counter(), time.process_time()
     for i in range(w.k - 1):
         st.accumulate(grads[i], weights[i], i == 0)
     st.unscale_check_norm(grads[-1], weights[-1], w.k == 1, w.max_norm)
     st.adamw_step(grads[-1], weights[-1], w.k == 1, **w.hp)
     st.scaler_update()
     dt_s = time.perf_counter() - t0
+    cpu_s = time.process_time() - c0            # CPU time of all threads of this process
     n_sample = sum(p[2] for p in pieces)
     # the same oracle on one thread, over one 16M-element segment
     j = max(range(len(pieces)), key=lambda i: pieces[i][2])
@@ -96,7 +97,9 @@ def cpu_baseline(w, seconds_hint=20.0):
     dt_1 = time.perf_counter() - t1
     return {"value": n_sample / dt_s, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": "%d params (%d tensors of the first layer, %d segments), k=%d, one full step, "
-                      "%.1f s" % (n_sample, len(sample), len(pieces), w.k, dt_s),
+                      "%.1f s wall, %.1f s of CPU time" % (n_sample, len(sample), len(pieces), w.k,
+                                                            dt_s, cpu_s),
+            "cpu_seconds": cpu_s,
             "single_thread": {"value": masters[j].size / dt_1, "unit": "params/s",
                               "sample": "one segment (%d params), %.2f s"
                                         % (masters[j].size, dt_1)}}
