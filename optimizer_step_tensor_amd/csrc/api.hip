@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -89,6 +90,19 @@ mp_status ok()
 mp_status hip_fail(hipError_t e, const char* what)
 {
     return fail(MP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Entry points that build host tables run their body through this, so that a
+// failed host allocation becomes MP_ERR_NOMEM instead of an exception crossing
+// the C ABI.
+template <class Body>
+mp_status guarded(Body&& body)
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc&) {
+        return fail(MP_ERR_NOMEM, "host allocation failed");
+    }
 }
 
 bool aligned16(const void* p)
@@ -271,62 +285,66 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
                          void* const* acc, void* const* master, void* const* m, void* const* v,
                          void* const* w16, const float* wd_mult, mp_plan** out)
 {
-    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
-    *out = nullptr;
-    if (n_tensors < 1) return fail(MP_ERR_INVALID, "n_tensors must be >= 1");
-    if (!valid_dtype(dtype)) return fail(MP_ERR_INVALID, "unknown dtype %d", (int)dtype);
-    if (numel == nullptr || master == nullptr || m == nullptr || v == nullptr || w16 == nullptr)
-        return fail(MP_ERR_INVALID, "numel, master, m, v and w16 arrays are required");
-    std::vector<TensorDesc> tensors(n_tensors);
-    std::vector<Chunk> chunks;
-    int64_t total = 0;
-    for (int32_t i = 0; i < n_tensors; ++i) {
-        if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
-            return fail(MP_ERR_INVALID, "tensor %d: numel %lld out of range", i, (long long)numel[i]);
-        void* ptrs[5] = {acc ? acc[i] : nullptr, master[i], m[i], v[i], w16[i]};
-        for (int k = 0; k < 5; ++k) {
-            if (k == 0 && acc == nullptr) continue;
-            if (ptrs[k] == nullptr) return fail(MP_ERR_INVALID, "tensor %d: NULL buffer", i);
-            if (!aligned16(ptrs[k])) return fail(MP_ERR_ALIGN, "tensor %d: buffer not 16-byte aligned", i);
+    return guarded([&]() -> mp_status {
+        if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+        *out = nullptr;
+        if (n_tensors < 1) return fail(MP_ERR_INVALID, "n_tensors must be >= 1");
+        if (!valid_dtype(dtype)) return fail(MP_ERR_INVALID, "unknown dtype %d", (int)dtype);
+        if (numel == nullptr || master == nullptr || m == nullptr || v == nullptr || w16 == nullptr)
+            return fail(MP_ERR_INVALID, "numel, master, m, v and w16 arrays are required");
+        std::vector<TensorDesc> tensors(n_tensors);
+        std::vector<Chunk> chunks;
+        int64_t total = 0;
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
+                return fail(MP_ERR_INVALID, "tensor %d: numel %lld out of range", i, (long long)numel[i]);
+            void* ptrs[5] = {acc ? acc[i] : nullptr, master[i], m[i], v[i], w16[i]};
+            for (int k = 0; k < 5; ++k) {
+                if (k == 0 && acc == nullptr) continue;
+                if (ptrs[k] == nullptr) return fail(MP_ERR_INVALID, "tensor %d: NULL buffer", i);
+                if (!aligned16(ptrs[k])) return fail(MP_ERR_ALIGN, "tensor %d: buffer not 16-byte aligned", i);
+            }
+            const float mult = wd_mult ? wd_mult[i] : 1.0f;
+            if (!std::isfinite(mult) || mult < 0.0f)
+                return fail(MP_ERR_INVALID, "tensor %d: wd_mult must be finite and >= 0", i);
+            tensors[i] = TensorDesc{static_cast<float*>(ptrs[0]), static_cast<float*>(ptrs[1]),
+                                    static_cast<float*>(ptrs[2]), static_cast<float*>(ptrs[3]),
+                                    static_cast<uint16_t*>(ptrs[4]), numel[i], mult, 0};
+            total += numel[i];
+            if (total > (int64_t(1) << 48))
+                return fail(MP_ERR_INVALID, "the plan holds more than 2^48 elements");
         }
-        const float mult = wd_mult ? wd_mult[i] : 1.0f;
-        if (!std::isfinite(mult) || mult < 0.0f)
-            return fail(MP_ERR_INVALID, "tensor %d: wd_mult must be finite and >= 0", i);
-        tensors[i] = TensorDesc{static_cast<float*>(ptrs[0]), static_cast<float*>(ptrs[1]),
-                                static_cast<float*>(ptrs[2]), static_cast<float*>(ptrs[3]),
-                                static_cast<uint16_t*>(ptrs[4]), numel[i], mult, 0};
-        total += numel[i];
-    }
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    const int cus = device_cus(device);
-    const int64_t grid_cap = MPK_ELEM_BLOCKS_PER_CU > 0 ? int64_t(cus) * MPK_ELEM_BLOCKS_PER_CU
-                                                         : int64_t(1) << 30;
-    const int32_t ch = build_chunks(n_tensors, numel, cus, chunks);
-    mp_plan* p = new (std::nothrow) mp_plan();
-    if (p == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
-    p->device = device;
-    p->n_tensors = n_tensors;
-    p->dtype = dtype;
-    p->has_acc = acc != nullptr;
-    p->total = total;
-    p->n_chunks = static_cast<int64_t>(chunks.size());
-    p->chunk_elems = ch;
-    p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
-    p->norm_grid = p->grid;
-    p->numel.assign(numel, numel + n_tensors);
-    // every partial sum is written by its block before any kernel reads it
-    const size_t partial_bytes = (static_cast<size_t>(p->norm_grid) + mpk::kNormStage2) * sizeof(double);
-    if ((e = upload(&p->d_tensors, tensors)) != hipSuccess ||
-        (e = upload(&p->d_chunks, chunks)) != hipSuccess ||
-        (e = hipMalloc(reinterpret_cast<void**>(&p->d_partials), partial_bytes)) != hipSuccess) {
-        mp_plan_destroy(p);
-        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
-                                        : hip_fail(e, "plan upload");
-    }
-    *out = p;
-    return ok();
+        int device = 0;
+        hipError_t e = hipGetDevice(&device);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        const int cus = device_cus(device);
+        const int64_t grid_cap = MPK_ELEM_BLOCKS_PER_CU > 0 ? int64_t(cus) * MPK_ELEM_BLOCKS_PER_CU
+                                                             : int64_t(1) << 30;
+        const int32_t ch = build_chunks(n_tensors, numel, cus, chunks);
+        mp_plan* p = new (std::nothrow) mp_plan();
+        if (p == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+        p->device = device;
+        p->n_tensors = n_tensors;
+        p->dtype = dtype;
+        p->has_acc = acc != nullptr;
+        p->total = total;
+        p->n_chunks = static_cast<int64_t>(chunks.size());
+        p->chunk_elems = ch;
+        p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
+        p->norm_grid = p->grid;
+        p->numel.assign(numel, numel + n_tensors);
+        // every partial sum is written by its block before any kernel reads it
+        const size_t partial_bytes = (static_cast<size_t>(p->norm_grid) + mpk::kNormStage2) * sizeof(double);
+        if ((e = upload(&p->d_tensors, tensors)) != hipSuccess ||
+            (e = upload(&p->d_chunks, chunks)) != hipSuccess ||
+            (e = hipMalloc(reinterpret_cast<void**>(&p->d_partials), partial_bytes)) != hipSuccess) {
+            mp_plan_destroy(p);
+            return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
+                                            : hip_fail(e, "plan upload");
+        }
+        *out = p;
+        return ok();
+    });
 }
 
 mp_status mp_plan_destroy(mp_plan* plan)
@@ -354,22 +372,24 @@ mp_status mp_chunk_layout(int32_t n_tensors, const int64_t* numel, int32_t n_cus
                           int32_t* chunk_elems, int64_t* n_chunks, int32_t* tensor_out,
                           int64_t* start_out, int32_t* len_out, int64_t capacity)
 {
-    if (n_tensors < 1 || numel == nullptr || n_cus < 1)
-        return fail(MP_ERR_INVALID, "need n_tensors >= 1, numel and n_cus >= 1");
-    for (int32_t i = 0; i < n_tensors; ++i)
-        if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
-            return fail(MP_ERR_INVALID, "tensor %d: numel out of range", i);
-    std::vector<Chunk> chunks;
-    const int32_t ch = build_chunks(n_tensors, numel, n_cus, chunks);
-    if (chunk_elems) *chunk_elems = ch;
-    if (n_chunks) *n_chunks = static_cast<int64_t>(chunks.size());
-    const int64_t n = std::min<int64_t>(capacity, static_cast<int64_t>(chunks.size()));
-    for (int64_t c = 0; c < n; ++c) {
-        if (tensor_out) tensor_out[c] = chunks[c].tensor;
-        if (start_out) start_out[c] = chunks[c].start;
-        if (len_out) len_out[c] = chunks[c].len;
-    }
-    return ok();
+    return guarded([&]() -> mp_status {
+        if (n_tensors < 1 || numel == nullptr || n_cus < 1)
+            return fail(MP_ERR_INVALID, "need n_tensors >= 1, numel and n_cus >= 1");
+        for (int32_t i = 0; i < n_tensors; ++i)
+            if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
+                return fail(MP_ERR_INVALID, "tensor %d: numel out of range", i);
+        std::vector<Chunk> chunks;
+        const int32_t ch = build_chunks(n_tensors, numel, n_cus, chunks);
+        if (chunk_elems) *chunk_elems = ch;
+        if (n_chunks) *n_chunks = static_cast<int64_t>(chunks.size());
+        const int64_t n = std::min<int64_t>(capacity, static_cast<int64_t>(chunks.size()));
+        for (int64_t c = 0; c < n; ++c) {
+            if (tensor_out) tensor_out[c] = chunks[c].tensor;
+            if (start_out) start_out[c] = chunks[c].start;
+            if (len_out) len_out[c] = chunks[c].len;
+        }
+        return ok();
+    });
 }
 
 namespace {
@@ -402,54 +422,58 @@ void free_gradset(mp_gradset* g)
 
 mp_status mp_gradset_create(const mp_plan* plan, void* const* g16, mp_gradset** out)
 {
-    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
-    *out = nullptr;
-    if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and g16 are required");
-    std::vector<uint16_t*> ptrs;
-    mp_status st = check_grad_ptrs(plan, g16, ptrs);
-    if (st != MP_OK) return st;
-    mp_gradset* g = new (std::nothrow) mp_gradset();
-    if (g == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
-    g->plan = plan;
-    hipError_t e = upload(&g->d_ptrs, ptrs);
-    const size_t slot_bytes = ptrs.size() * sizeof(uint16_t*);
-    for (int i = 0; i < kGradsetSlots && e == hipSuccess; ++i) {
-        e = hipHostMalloc(reinterpret_cast<void**>(&g->h_slots[i]), slot_bytes, hipHostMallocDefault);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&g->copied[i], hipEventDisableTiming);
-    }
-    if (e != hipSuccess) {
-        free_gradset(g);
-        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "allocation failed")
-                                        : hip_fail(e, "gradset upload");
-    }
-    *out = g;
-    return ok();
+    return guarded([&]() -> mp_status {
+        if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+        *out = nullptr;
+        if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and g16 are required");
+        std::vector<uint16_t*> ptrs;
+        mp_status st = check_grad_ptrs(plan, g16, ptrs);
+        if (st != MP_OK) return st;
+        mp_gradset* g = new (std::nothrow) mp_gradset();
+        if (g == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+        g->plan = plan;
+        hipError_t e = upload(&g->d_ptrs, ptrs);
+        const size_t slot_bytes = ptrs.size() * sizeof(uint16_t*);
+        for (int i = 0; i < kGradsetSlots && e == hipSuccess; ++i) {
+            e = hipHostMalloc(reinterpret_cast<void**>(&g->h_slots[i]), slot_bytes, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&g->copied[i], hipEventDisableTiming);
+        }
+        if (e != hipSuccess) {
+            free_gradset(g);
+            return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "allocation failed")
+                                            : hip_fail(e, "gradset upload");
+        }
+        *out = g;
+        return ok();
+    });
 }
 
 mp_status mp_gradset_update(mp_gradset* set, void* const* g16, mp_stream stream)
 {
-    if (set == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "gradset and g16 are required");
-    std::vector<uint16_t*> ptrs;
-    mp_status st = check_grad_ptrs(set->plan, g16, ptrs);
-    if (st == MP_OK) st = check_device(set->plan->device, "the gradset's plan");
-    if (st != MP_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    hipError_t e = hipStreamIsCapturing(s, &cap);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-    if (cap != hipStreamCaptureStatusNone)
-        return fail(MP_ERR_INVALID, "mp_gradset_update cannot be captured in a graph: a replay "
-                                    "would copy whatever the staging slot holds then");
-    const int slot = set->next_slot;
-    e = hipEventSynchronize(set->copied[slot]);     // the copy that last read this slot has run
-    if (e != hipSuccess) return hip_fail(e, "gradset slot wait");
-    std::memcpy(set->h_slots[slot], ptrs.data(), ptrs.size() * sizeof(uint16_t*));
-    e = hipMemcpyAsync(set->d_ptrs, set->h_slots[slot], ptrs.size() * sizeof(uint16_t*),
-                       hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipEventRecord(set->copied[slot], s);
-    if (e != hipSuccess) return hip_fail(e, "gradset update");
-    set->next_slot = (slot + 1) % kGradsetSlots;
-    return ok();
+    return guarded([&]() -> mp_status {
+        if (set == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "gradset and g16 are required");
+        std::vector<uint16_t*> ptrs;
+        mp_status st = check_grad_ptrs(set->plan, g16, ptrs);
+        if (st == MP_OK) st = check_device(set->plan->device, "the gradset's plan");
+        if (st != MP_OK) return st;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(s, &cap);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone)
+            return fail(MP_ERR_INVALID, "mp_gradset_update cannot be captured in a graph: a replay "
+                                        "would copy whatever the staging slot holds then");
+        const int slot = set->next_slot;
+        e = hipEventSynchronize(set->copied[slot]);     // the copy that last read this slot has run
+        if (e != hipSuccess) return hip_fail(e, "gradset slot wait");
+        std::memcpy(set->h_slots[slot], ptrs.data(), ptrs.size() * sizeof(uint16_t*));
+        e = hipMemcpyAsync(set->d_ptrs, set->h_slots[slot], ptrs.size() * sizeof(uint16_t*),
+                           hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipEventRecord(set->copied[slot], s);
+        if (e != hipSuccess) return hip_fail(e, "gradset update");
+        set->next_slot = (slot + 1) % kGradsetSlots;
+        return ok();
+    });
 }
 
 mp_status mp_gradset_destroy(mp_gradset* set)
@@ -462,41 +486,43 @@ mp_status mp_gradset_destroy(mp_gradset* set)
 mp_status mp_fp8set_create(const mp_plan* plan, void* const* codes, void* const* scales,
                            mp_fp8set** out)
 {
-    if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
-    *out = nullptr;
-    if (plan == nullptr || codes == nullptr || scales == nullptr)
-        return fail(MP_ERR_INVALID, "plan, codes and scales are required");
-    std::vector<Fp8Out> outs(plan->n_tensors);
-    int32_t n_cast = 0;
-    for (int32_t i = 0; i < plan->n_tensors; ++i) {
-        if (codes[i] == nullptr && scales[i] == nullptr) {
-            outs[i] = Fp8Out{nullptr, nullptr};
-            continue;
+    return guarded([&]() -> mp_status {
+        if (out == nullptr) return fail(MP_ERR_INVALID, "out is NULL");
+        *out = nullptr;
+        if (plan == nullptr || codes == nullptr || scales == nullptr)
+            return fail(MP_ERR_INVALID, "plan, codes and scales are required");
+        std::vector<Fp8Out> outs(plan->n_tensors);
+        int32_t n_cast = 0;
+        for (int32_t i = 0; i < plan->n_tensors; ++i) {
+            if (codes[i] == nullptr && scales[i] == nullptr) {
+                outs[i] = Fp8Out{nullptr, nullptr};
+                continue;
+            }
+            if (codes[i] == nullptr || scales[i] == nullptr)
+                return fail(MP_ERR_INVALID, "tensor %d: codes and scales must both be set or both NULL", i);
+            if (plan->numel[i] % 16 != 0)
+                return fail(MP_ERR_INVALID, "tensor %d: numel %lld is not a multiple of 16", i,
+                            (long long)plan->numel[i]);
+            if (!aligned16(codes[i]) || (reinterpret_cast<uintptr_t>(scales[i]) & 3u) != 0)
+                return fail(MP_ERR_ALIGN, "tensor %d: codes must be 16-byte aligned, scales 4-byte aligned", i);
+            outs[i] = Fp8Out{static_cast<uint8_t*>(codes[i]), static_cast<float*>(scales[i])};
+            ++n_cast;
         }
-        if (codes[i] == nullptr || scales[i] == nullptr)
-            return fail(MP_ERR_INVALID, "tensor %d: codes and scales must both be set or both NULL", i);
-        if (plan->numel[i] % 16 != 0)
-            return fail(MP_ERR_INVALID, "tensor %d: numel %lld is not a multiple of 16", i,
-                        (long long)plan->numel[i]);
-        if (!aligned16(codes[i]) || (reinterpret_cast<uintptr_t>(scales[i]) & 3u) != 0)
-            return fail(MP_ERR_ALIGN, "tensor %d: codes must be 16-byte aligned, scales 4-byte aligned", i);
-        outs[i] = Fp8Out{static_cast<uint8_t*>(codes[i]), static_cast<float*>(scales[i])};
-        ++n_cast;
-    }
-    if (n_cast == 0) return fail(MP_ERR_INVALID, "no tensor has FP8 outputs");
-    mp_status st = check_device(plan->device, "the plan");
-    if (st != MP_OK) return st;
-    mp_fp8set* f = new (std::nothrow) mp_fp8set();
-    if (f == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
-    f->plan = plan;
-    hipError_t e = upload(&f->d_out, outs);
-    if (e != hipSuccess) {
-        delete f;
-        return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
-                                        : hip_fail(e, "fp8 set upload");
-    }
-    *out = f;
-    return ok();
+        if (n_cast == 0) return fail(MP_ERR_INVALID, "no tensor has FP8 outputs");
+        mp_status st = check_device(plan->device, "the plan");
+        if (st != MP_OK) return st;
+        mp_fp8set* f = new (std::nothrow) mp_fp8set();
+        if (f == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
+        f->plan = plan;
+        hipError_t e = upload(&f->d_out, outs);
+        if (e != hipSuccess) {
+            delete f;
+            return e == hipErrorOutOfMemory ? fail(MP_ERR_NOMEM, "device allocation failed")
+                                            : hip_fail(e, "fp8 set upload");
+        }
+        *out = f;
+        return ok();
+    });
 }
 
 mp_status mp_fp8set_destroy(mp_fp8set* set)

@@ -126,6 +126,12 @@ def test_validation_before_any_device_work(mp):
     assert "aligned" in mp.mp_last_error()
     zero = (ctypes.c_int64 * 1)(0)
     assert L.mp_plan_create(1, zero, 0, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    # more than 2^48 elements in one plan is refused before any allocation
+    big_n = 300
+    big = (ctypes.c_int64 * big_n)(*([2 ** 40] * big_n))
+    gp = ctypes.cast((ctypes.c_void_p * big_n)(*([0x10000] * big_n)), PP)
+    assert L.mp_plan_create(big_n, big, 0, None, gp, gp, gp, gp, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert "2^48" in mp.mp_last_error()
     neg = (ctypes.c_float * 1)(-1.0)
     assert L.mp_plan_create(1, ne, 0, None, g, g, g, g, neg, ctypes.byref(out)) == mp.MP_ERR_INVALID
     for cfg in (mp.scaler_cfg(init_scale=3.0), mp.scaler_cfg(growth=0.5), mp.scaler_cfg(backoff=2.0),
