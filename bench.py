@@ -186,11 +186,29 @@ def time_fused_fp8(mp, torch, w, model, sets, state, hp, weights, stream, reps=3
             "frac": fused_bytes / ms["fused"] / 1e6 / HBM_PEAK_GBPS}
 
 
+def time_save_restore(mp, torch, state, stream, reps=20):
+    """Export of the device state into pinned host memory (enqueue + wait) and import of the
+    blob back (validated on the host, copied, waited for), host wall time per call."""
+    blob = torch.empty(mp.MP_STATE_BLOB_BYTES, dtype=torch.uint8, pin_memory=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        mp.mp_state_export(state, blob.data_ptr(), mp.MP_STATE_BLOB_BYTES, stream)
+        stream.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(reps):
+        mp.mp_state_import(state, blob.data_ptr(), mp.MP_STATE_BLOB_BYTES, stream)
+    t2 = time.perf_counter()
+    return {"blob_bytes": mp.MP_STATE_BLOB_BYTES, "export_us": (t1 - t0) / reps * 1e6,
+            "import_us": (t2 - t1) / reps * 1e6}
+
+
 def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
     """The rows after the hot path, on the same resident buffers:
     - the fine-grained FP8 cast (block 16) of every fp32 master;
     - the same cast fused into the AdamW pass (mp_adamw_step_fp8), against the plain AdamW pass
       timed the same way in alternation;
+    - saving and restoring the device state (scaler and optimizer clock);
     - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
       multiples of 8 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
     out = {}
@@ -219,6 +237,7 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
                              "bytes_per_element": 5.25, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
     del codes, scales
     out["adamw_fp8_fused"] = time_fused_fp8(mp, torch, w, model, sets, state, hp, weights, stream)
+    out["state_save_restore"] = time_save_restore(mp, torch, state, stream)
     ranks, r = 8, 0
     numel, ptrs = [], {"acc": [], "master": [], "m": [], "v": [], "w16": []}
     gp = [[] for _ in range(k)]
