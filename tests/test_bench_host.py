@@ -1,0 +1,45 @@
+"""bench.py's byte accounting on the host (no GPU): the algorithmic bytes per parameter that
+the roofline and the step GB/s are computed from.
+
+A step with k micro-batches reads and writes 10k + 24 bytes per parameter when the last
+micro-batch is folded into the norm and AdamW passes (k >= 2): 6 for the first
+accumulation, 10 for each further one, 6 for the norm (fp32 accumulator + 16-bit last
+gradient) and 32 for AdamW (18 read, 14 written).  With one micro-batch there is no
+accumulator: the norm reads the 16-bit gradient (2) and AdamW 28 bytes, 30 in all.  The
+model state itself is 16 bytes per parameter ('Chapter 41 Training at Scale', equation 41.1)
+plus the 4-byte accumulator.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_step_bytes_follow_the_schedule():
+    for k in (2, 3, 4, 8, 16):
+        b = bench.bytes_per_param(k)
+        assert b["step"] == 10 * k + 24
+        assert b["step"] == b["accumulate_first"] + (k - 2) * b["accumulate"] + b["norm"] + b["adamw"]
+        assert b["adamw"] == 32 and b["norm"] == 6
+    b1 = bench.bytes_per_param(1)
+    assert b1["step"] == 30 and b1["norm"] + b1["adamw"] == 30 and b1["adamw"] == 28
+
+
+def test_adamw_bytes_are_the_state_it_touches():
+    """AdamW reads acc (4), the last 16-bit gradient (2), master, m, v (12) and writes master, m,
+    v (12) and the 16-bit weight (2): every byte of the 20-byte state except the gradient buffers
+    of the other micro-batches, once."""
+    b = bench.bytes_per_param(4)
+    read = 4 + 2 + 4 + 4 + 4
+    written = 4 + 4 + 4 + 2
+    assert b["adamw"] == read + written == 32
+
+
+def test_more_than_one_gpu_is_refused_without_touching_a_gpu():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "4"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and r.stdout == ""
