@@ -31,7 +31,7 @@ class OracleRun:
         sc = (oracle.make_scaler(**w.scaler) if w.scaler is not None
               else oracle.make_scaler(init_scale=1.0, enabled=False))
         self.st = oracle.OracleStep(dt, masters, w16, scaler=sc, with_acc=w.k > 1,
-                                    threads=threads)
+                                    wd_mult=getattr(w, "wd_mult", None), threads=threads)
         self.step_no = 0
 
     def grads(self, step, micro):
@@ -70,7 +70,8 @@ class DeviceRun:
         import optimizer_step_tensor_amd as mp
         self.torch, self.mp, self.w = torch, mp, w
         dt = mp.MP_BF16 if w.dtype == inputs.BF16 else mp.MP_FP16
-        self.model = mp.ModelState(w.numels, dt, with_acc=w.k > 1, layout=layout)
+        self.model = mp.ModelState(w.numels, dt, with_acc=w.k > 1, layout=layout,
+                                   wd_mult=getattr(w, "wd_mult", None))
         for t, x in enumerate(self.model.master):
             inputs.fill_dev_f32(x, w.master_recipe(t))
         for x, y in zip(self.model.master, self.model.w16):

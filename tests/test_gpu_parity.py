@@ -151,6 +151,34 @@ def test_update_step_in_one_call(mp, name):
         dev.close()
 
 
+def test_weight_decay_multipliers(mp):
+    """Per-tensor decay multipliers ('Accumulate gradients and recompute activations': decoupled
+    decay; a caller may exempt tensors): norm vectors exempt, the embedding and head at half,
+    every matrix at 1.  The device equals the oracle on every step."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make("llama3-8B-small")
+    w.wd_mult = [0.0 if len(shape) == 1 else (0.5 if name in ("tok_embed", "lm_head") else 1.0)
+                 for name, shape in w.tensors]
+    assert 0.0 in w.wd_mult and 0.5 in w.wd_mult and 1.0 in w.wd_mult
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            say("  step", s, compare_step(dev, orc, w, s))
+        # an exempt tensor moved by the Adam term alone: it differs from a decayed run
+        t = w.wd_mult.index(0.0)
+        plain = configs.make("llama3-8B-small")
+        ref = OracleRun(plain)
+        for _ in range(w.steps):
+            ref.step()
+        assert not (ref.st.masters[t] == dev.host("master")[t]).all()
+    finally:
+        dev.close()
+
+
 def test_norm_is_deterministic(mp):
     """The same inputs give the same sum of squares, bit for bit, on every run."""
     from harness import DeviceRun
