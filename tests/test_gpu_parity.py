@@ -179,6 +179,36 @@ def test_weight_decay_multipliers(mp):
         dev.close()
 
 
+def test_scaler_clamps_at_min_and_max(mp):
+    """The controller's bounds ('Megatron Internals III', section 5: a floor on the scale; a cap
+    on growth): S starts at 2 with growth every clean step, is capped at 4, then three overflows
+    in a row halve it to 2 and 1 and hold it at the floor of 1; a clean step grows it again.  The
+    device's overflow flag, skip, S and count equal the oracle's on every step."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make("edges-fp16")
+    w.scaler = dict(init_scale=2.0, growth=2.0, backoff=0.5, min_scale=1.0, max_scale=4.0,
+                    interval=1)
+    bad_steps = (3, 4, 5)
+    w.injection = lambda step: (1, 2) if step in bad_steps else None
+    w.steps = 6
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    trace = []
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            st = dev.stats()
+            assert st["found_inf"] == int(s in bad_steps) == int(orc.st.found_inf), s
+            assert st["scale"] == orc.st.scaler.scale and st["good_steps"] == orc.st.scaler.good_steps
+            trace.append(st["scale"])
+            say("  step", s, compare_step(dev, orc, w, s))
+        assert trace == [4.0, 4.0, 2.0, 1.0, 1.0, 2.0]
+    finally:
+        dev.close()
+
+
 def test_norm_is_deterministic(mp):
     """The same inputs give the same sum of squares, bit for bit, on every run."""
     from harness import DeviceRun
