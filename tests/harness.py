@@ -33,6 +33,7 @@ class OracleRun:
         self.st = oracle.OracleStep(dt, masters, w16, scaler=sc, with_acc=w.k > 1,
                                     wd_mult=getattr(w, "wd_mult", None), threads=threads)
         self.step_no = 0
+        self.fold_last = True              # False: accumulate every micro-batch, then norm/AdamW
 
     def grads(self, step, micro):
         S = self.st.scaler.scale
@@ -51,6 +52,14 @@ class OracleRun:
         self.prev_master = [x.copy() for x in st.masters]
         self.prev_m = [x.copy() for x in st.m]
         weights = oracle.token_weights(w.token_counts(s))
+        if not self.fold_last:
+            for i in range(w.k):
+                st.accumulate(self.grads(s, i), weights[i], i == 0)
+            acc_snapshot = [a.copy() for a in st.acc]
+            st.unscale_check_norm(None, 1.0, False, w.max_norm)
+            st.adamw_step(None, 1.0, False, **w.hp)
+            st.scaler_update()
+            return acc_snapshot
         for i in range(w.k - 1):
             st.accumulate(self.grads(s, i), weights[i], i == 0)
         acc_snapshot = [a.copy() for a in st.acc] if st.acc is not None else None
@@ -86,6 +95,7 @@ class DeviceRun:
         self.step_no = 0
         self.fp8set = None                 # set: steps use the fused AdamW + FP8 entry point
         self.one_call = False              # True: steps use mp_update_step
+        self.fold_last = True              # False: accumulate every micro-batch, then norm/AdamW
 
     def stats(self):
         return self.mp.read_stats(self.state)
@@ -109,6 +119,14 @@ class DeviceRun:
         assert len(self.g16) == w.k, "per-micro-batch buffers needed to run a step"
         self.fill_grads(s, scale)
         weights = mp.mp_token_weights(w.token_counts(s))
+        if not self.fold_last:
+            for i in range(w.k):
+                mp.mp_accumulate(self.model.plan, self.gsets[i], weights[i], i == 0)
+            acc_snapshot = [a.cpu().numpy() for a in self.model.acc] if snapshot else None
+            mp.mp_unscale_check_norm(self.model.plan, self.state, None, 1.0, 0, w.max_norm)
+            mp.mp_adamw_step(self.model.plan, self.state, None, 1.0, 0, self.hp)
+            mp.mp_scaler_update(self.state)
+            return acc_snapshot
         for i in range(w.k - 1):
             mp.mp_accumulate(self.model.plan, self.gsets[i], weights[i], i == 0)
         acc_snapshot = ([a.cpu().numpy() for a in self.model.acc]

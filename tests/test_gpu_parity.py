@@ -209,6 +209,26 @@ def test_scaler_clamps_at_min_and_max(mp):
         dev.close()
 
 
+@pytest.mark.parametrize("name", ["edges", "edges-fp16", "gpt-1.3B-small"])
+def test_unfolded_schedule(mp, name):
+    """Every micro-batch accumulated first, then the norm and AdamW reading the accumulator alone
+    (no last micro-batch folded in, last = NULL): the accumulator after the k-th pass and every
+    step equal the oracle, in bf16 and in fp16 with an overflow."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make(name)
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    orc.fold_last = dev.fold_last = False
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            acc_o = orc.step()
+            acc_d = dev.step(scale, snapshot=True)
+            say("  step", s, compare_step(dev, orc, w, s, acc_d, acc_o))
+    finally:
+        dev.close()
+
+
 def test_norm_is_deterministic(mp):
     """The same inputs give the same sum of squares, bit for bit, on every run."""
     from harness import DeviceRun
