@@ -16,6 +16,7 @@ sample.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--graph] [--gpus 1]
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -350,12 +351,21 @@ def main():
         del a, b
 
     ev = {name: [] for name in ("accumulate", "norm", "adamw", "fused")}
+    # every timing event is created, and recorded once so that its HIP event exists, before
+    # any timed region; the timed steps then only record them
+    pool = [torch.cuda.Event(enable_timing=True)
+            for _ in range(args.steps * (2 * k + 6) + 2)]
+    for e in pool:
+        e.record(stream)
+    torch.cuda.synchronize()
+    pool.reverse()
+    take = pool.pop
 
     def one_step_on(stream, record):
         def timed(name, fn):
             if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0 = take()
+                e1 = take()
                 e0.record(stream)
                 fn()
                 e1.record(stream)
@@ -367,7 +377,7 @@ def main():
             timed("accumulate", lambda i=i: mp.mp_accumulate(plan, sets[i], weights[i], i == 0,
                                                              stream))
         if record:                            # the fused step: norm + AdamW + scaler
-            f0 = torch.cuda.Event(enable_timing=True)
+            f0 = take()
             f0.record(stream)
         timed("norm", lambda: mp.mp_unscale_check_norm(plan, state, sets[-1], weights[-1], lif,
                                                        w.max_norm, stream))
@@ -375,7 +385,7 @@ def main():
                                                 stream))
         mp.mp_scaler_update(state, stream)
         if record:
-            f1 = torch.cuda.Event(enable_timing=True)
+            f1 = take()
             f1.record(stream)
             ev["fused"].append((f0, f1))
 
@@ -410,13 +420,15 @@ def main():
     # on, inside the timed region; a replayed graph cannot, so after a graph run the same
     # number of eager steps is timed with events outside it
     record = graph is None
+    gc.collect()
+    gc.disable()                              # no collector pauses inside the timed region
     if args.cold:
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         step_ms = []
         for _ in range(args.steps):
             flush.fill_(1.0)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a = take()
+            b = take()
             a.record(stream)
             one_step(record)
             b.record(stream)
@@ -427,7 +439,7 @@ def main():
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        bounds = [take() for _ in range(args.steps + 1)]
         bounds[0].record(stream)
         for i in range(args.steps):
             one_step(record)
@@ -445,6 +457,7 @@ def main():
         for _ in range(args.steps):
             one_step_on(stream, True)
     torch.cuda.synchronize()
+    gc.enable()
     kernel_ms = {n: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None)
                  for n, v in ev.items()}
     adam_bytes = bpp["adamw"] * P
