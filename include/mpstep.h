@@ -140,8 +140,9 @@ mp_status mp_token_weights(int32_t k, const int64_t* counts, float* weights_out)
  * The 16-bit weight and gradient are 2 bytes in both formats. */
 size_t mp_state_bytes_per_param(mp_dtype16 dtype, int32_t with_accumulator);
 
-/* Describe the parameter tensors of one model.  For tensor i (numel[i] >= 1
- * elements, contiguous): acc[i] fp32 accumulation buffer, master[i] fp32
+/* Describe the parameter tensors of one model.  For tensor i (1 <= numel[i]
+ * <= 2^40 elements, contiguous; at most 2^48 in all): acc[i] fp32
+ * accumulation buffer, master[i] fp32
  * master weight, m[i] and v[i] fp32 Adam moments, w16[i] the 16-bit model
  * weight.  `acc` may be NULL when the model is never accumulated (one
  * micro-batch per update: pass it as the last micro-batch with
@@ -235,8 +236,9 @@ mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int3
  * (last_is_first != 0), or fl(acc + fl(w_last * widen(last))) -- the last
  * micro-batch folded in exactly as mp_accumulate would add it.  Then
  *   g = fl(g_eff * (1/S));  found_inf = any g is inf or NaN;
- *   sumsq = sum g^2 in binary64 (fixed-order two-stage reduction, the same
- *           bits on every run);  grad_norm = fp32(sqrt(sumsq));
+ *   sumsq = sum g^2 in binary64 (a fixed-order reduction: per chunk, then
+ *           256 contiguous range sums, then one total; the same bits on
+ *           every run);  grad_norm = fp32(sqrt(sumsq));
  *   clip_coef = min(1, fl(max_norm / fl(grad_norm + 1e-6))) if max_norm > 0
  *               and !found_inf, else 1.
  * Results stay on the device for mp_adamw_step and mp_state_read. */
