@@ -9,7 +9,8 @@ from inputs import configs
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_equal_eager_steps():
+@pytest.mark.parametrize("form", ["separate calls", "mp_update_step"])
+def test_graph_replays_equal_eager_steps(form):
     import torch
     import optimizer_step_tensor_amd as mp
     from harness import DeviceRun
@@ -22,6 +23,10 @@ def test_graph_replays_equal_eager_steps():
         plan = dev.model.plan
         for i in range(k - 1):
             mp.mp_accumulate(plan, dev.gsets[i], weights[i], i == 0, stream)
+        if form == "mp_update_step":
+            mp.mp_update_step(plan, dev.state, dev.gsets[-1], weights[-1], 0, w.max_norm, dev.hp,
+                              stream)
+            return
         mp.mp_unscale_check_norm(plan, dev.state, dev.gsets[-1], weights[-1], 0, w.max_norm, stream)
         mp.mp_adamw_step(plan, dev.state, dev.gsets[-1], weights[-1], 0, dev.hp, stream)
         mp.mp_scaler_update(dev.state, stream)
