@@ -19,7 +19,8 @@ Workloads (ids are stream labels):
 * 13, 14, 15: reduced versions of 3, 4 and 5 for element-by-element parity;
   16, 17, 19: lists of edge-case sizes around the kernels' tile boundaries (bf16; fp16 with
   a dynamic scale and an injected overflow; the same on sizes that are multiples of 16);
-  18: the fp16 run's scaler over 2003 steps on three small tensors.
+  18: the fp16 run's scaler over 2003 steps on three small tensors;
+  20: one tensor of 2^31 + 4097 elements and one of 7.
 """
 import math
 
@@ -163,6 +164,10 @@ def make(name):
         return Workload(19, name, [("b%02d" % i, (n,)) for i, n in enumerate(sizes)], FP16, 2,
                         grad_kind=LOGUNIF_MIX, tail_prob=0.05, lo_exp=-30, hi_exp=-20,
                         scaler=dict(FP16_SCALER, interval=2), inject_step=2, steps=5)
+    if name == "huge-tensor":
+        # one tensor past 2^31 elements (element offsets that need 64 bits everywhere: chunk
+        # starts, pointers, generator indices) next to a tiny one; bf16, k = 2
+        return Workload(20, name, [("big", (2 ** 31 + 4097,)), ("small", (7,))], BF16, 2, steps=2)
     if name == "gpt-124M-scaler":
         # the fp16 run's scaler, overflow and gradient recipe on a small tensor list, long enough
         # for the scale to grow back: 2000 clean steps after the overflow of step 3

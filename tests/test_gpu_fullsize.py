@@ -22,7 +22,8 @@ def say(*a):
 
 
 @pytest.mark.timeout(1100)
-@pytest.mark.parametrize("name,steps", [("ragged-4096", 2), ("gpt-1.3B", 2), ("llama3-8B", 2)])
+@pytest.mark.parametrize("name,steps", [("ragged-4096", 2), ("gpt-1.3B", 2), ("llama3-8B", 2),
+                                        ("huge-tensor", 2)])
 def test_full_size_sampled_parity(name, steps):
     run_sampled_parity(name, steps)
 
