@@ -151,6 +151,26 @@ def test_update_step_in_one_call(mp, name):
         dev.close()
 
 
+def test_single_micro_batch_bf16(mp):
+    """bf16 with one micro-batch: no accumulator at all, the norm and AdamW read the 16-bit
+    gradient directly (weight n/N = 1).  Equal to the oracle on every step."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make("llama3-8B-small")
+    w.k = 1
+    w.steps = 3
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    assert dev.model.acc is None
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            say("  step", s, compare_step(dev, orc, w, s))
+    finally:
+        dev.close()
+
+
 def test_weight_decay_multipliers(mp):
     """Per-tensor decay multipliers ('Accumulate gradients and recompute activations': decoupled
     decay; a caller may exempt tensors): norm vectors exempt, the embedding and head at half,
