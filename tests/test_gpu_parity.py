@@ -151,6 +151,33 @@ def test_update_step_in_one_call(mp, name):
         dev.close()
 
 
+def test_random_hyperparameters(mp):
+    """Eight seeded AdamW configurations far from the defaults (lr 1e-6..1, beta1 0..0.999,
+    beta2 0..0.9999, eps 1e-12..1e-2, weight decay 0..0.5, clipping off or at 0.1..10) on the
+    bf16 edge list: the device equals the oracle on every step of every configuration, so the
+    operation order holds in every numeric regime these reach."""
+    import numpy as np
+    from harness import OracleRun, DeviceRun, compare_step
+    rng = np.random.default_rng(2026)
+    for c in range(8):
+        w = configs.make("edges")
+        w.hp = dict(lr=float(10 ** rng.uniform(-6, 0)), beta1=float(rng.choice([0.0, 0.5, 0.9, 0.999])),
+                    beta2=float(rng.choice([0.0, 0.9, 0.999, 0.9999])),
+                    eps=float(10 ** rng.uniform(-12, -2)), weight_decay=float(rng.uniform(0, 0.5)))
+        w.max_norm = float(rng.choice([0.0, 0.1, 1.0, 10.0]))
+        orc = OracleRun(w)
+        dev = DeviceRun(w)
+        try:
+            for s in range(1, w.steps + 1):
+                scale = orc.st.scaler.scale
+                orc.step()
+                dev.step(scale)
+                rep = compare_step(dev, orc, w, s)
+            say("  config", c, w.hp, "max_norm", w.max_norm, rep)
+        finally:
+            dev.close()
+
+
 def test_single_micro_batch_bf16(mp):
     """bf16 with one micro-batch: no accumulator at all, the norm and AdamW read the 16-bit
     gradient directly (weight n/N = 1).  Equal to the oracle on every step."""
