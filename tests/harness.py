@@ -4,13 +4,13 @@ Both sides read the same seeded inputs (``inputs``): the device side fills its
 buffers with the generator's HIP twin, the oracle side with its host twin.
 Nothing flows from the HIP path into the oracle.  The update schedule is the
 same on both sides: micro-batches 1..k-1 accumulated, the last one folded into
-the norm and update passes.
+the norm and update passes (or, with ``fold_last = False`` on both, all k
+accumulated and the norm and update reading the accumulator alone).
 """
 import numpy as np
 
 import inputs
 import oracle
-from inputs import configs
 
 
 def oracle_dtype(w):

@@ -1,7 +1,6 @@
 """The step is stream-ordered with no host synchronisation, so a whole step can be captured in a
 HIP graph (through torch.cuda.graph) and replayed (needs a GPU).  Every replay is checked
 against the same step run eagerly, with eager work and synchronisations between replays."""
-import numpy as np
 import pytest
 
 from inputs import configs
