@@ -136,6 +136,19 @@ int32_t mp_abi_version(void);
  * MP_ERR_INVALID if k < 1, any n_i <= 0, or N > 2^53. */
 mp_status mp_token_weights(int32_t k, const int64_t* counts, float* weights_out);
 
+/* mp_token_weights on the device, for counts that the data pipeline leaves in
+ * device memory: no host round trip, and a captured graph reads the counts of
+ * each replay.  `counts` (k int64, 8-byte aligned) and `weights_out` (k fp32,
+ * 4-byte aligned) are device pointers owned by the caller; one small kernel on
+ * `stream` writes weights_out[i] = fp32(n_i / N) with the same binary64
+ * division as the host call, so both give the same bits.  Counts the host call
+ * would refuse (any n_i <= 0, N > 2^53) cannot be refused here without a
+ * sync: every weight is then NaN, the gradient they scale is non-finite, and
+ * the step is skipped and the scale backed off exactly as on an overflow.
+ * MP_ERR_INVALID if k < 1 or a pointer is NULL, MP_ERR_ALIGN if misaligned. */
+mp_status mp_token_weights_dev(int32_t k, const int64_t* counts, float* weights_out,
+                               mp_stream stream);
+
 /* Model-state bytes per parameter ("Chapter 41 Training at Scale", equation
  * (41.1)): 16-bit weight 2 + 16-bit gradient 2 + fp32 master 4 + m 4 + v 4 =
  * 16, plus 4 for the fp32 accumulation buffer when with_accumulator != 0.
@@ -232,6 +245,13 @@ mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale);
 mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
                         mp_stream stream);
 
+/* mp_accumulate with the weight read on the device from *weight (fp32, 4-byte
+ * aligned device memory, e.g. an element of mp_token_weights_dev's output),
+ * when the kernel runs.  The value is not checked on the host: a non-finite
+ * weight makes the step overflow and be skipped. */
+mp_status mp_accumulate_dw(mp_plan* plan, const mp_gradset* g16, const float* weight,
+                           int32_t first, mp_stream stream);
+
 /* Unscale, check and measure ("Megatron Internals III", sections 4, 6 and 9;
  * "Mixed precision ...", section 2 "Dynamic scaling").  The gradient of each
  * element is g_eff = acc (last == NULL), fl(w_last * widen(last))
@@ -303,6 +323,14 @@ mp_status mp_scaler_update(mp_state* state, mp_stream stream);
 mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
                          int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
                          mp_stream stream);
+
+/* mp_update_step with w_last read on the device from *w_last (fp32, 4-byte
+ * aligned device memory), as in mp_accumulate_dw; the norm and the AdamW pass
+ * read the same address, so they see the same value.  w_last may be NULL only
+ * when last is NULL. */
+mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                            const float* w_last, int32_t last_is_first, float max_norm,
+                            const mp_adamw_hparams* hp, mp_stream stream);
 
 /* Elementwise casts with the step's conversions: dst = round-to-nearest-even
  * of src into the 16-bit format (as in mp_adamw_step), and dst = exact fp32

@@ -31,7 +31,8 @@ ENTRY_POINTS = [
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
-    "mp_gradset_update", "mp_update_step",
+    "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_dw",
+    "mp_update_step_dw",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -118,6 +119,9 @@ def _bind(L):
         "mp_adamw_step_fp8": ([P, P, P, f32, i32, ctypes.POINTER(AdamWHparams), P, P], i32),
         "mp_gradset_update": ([P, PP, P], i32),
         "mp_update_step": ([P, P, P, f32, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
+        "mp_token_weights_dev": ([i32, P, P, P], i32),
+        "mp_accumulate_dw": ([P, P, P, i32, P], i32),
+        "mp_update_step_dw": ([P, P, P, P, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -147,6 +151,13 @@ def _ptrs(values):
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
 
 
+def _addr(x):
+    """Device address of a tensor (or an int address); None stays NULL."""
+    if x is None:
+        return None
+    return ctypes.c_void_p(x.data_ptr() if isinstance(x, torch.Tensor) else int(x))
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -174,6 +185,12 @@ def mp_token_weights(counts):
     w = (ctypes.c_float * len(counts))()
     _check(lib().mp_token_weights(len(counts), n, w))
     return list(w)
+
+
+def mp_token_weights_dev(k, counts, weights_out, stream=None):
+    """counts: k int64 on the device; weights_out: k fp32 on the device."""
+    _check(lib().mp_token_weights_dev(int(k), _addr(counts), _addr(weights_out),
+                                      _stream(stream)))
 
 
 def mp_state_bytes_per_param(dtype, with_accumulator):
@@ -255,6 +272,12 @@ def mp_accumulate(plan, gradset, weight, first, stream=None):
     _check(lib().mp_accumulate(plan, gradset, float(weight), int(bool(first)), _stream(stream)))
 
 
+def mp_accumulate_dw(plan, gradset, weight, first, stream=None):
+    """weight: the device address of one fp32 (a tensor element or an int)."""
+    _check(lib().mp_accumulate_dw(plan, gradset, _addr(weight), int(bool(first)),
+                                  _stream(stream)))
+
+
 def mp_unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream=None):
     _check(lib().mp_unscale_check_norm(plan, state, last, float(w_last), int(bool(last_is_first)),
                                        float(max_norm), _stream(stream)))
@@ -268,6 +291,12 @@ def mp_adamw_step(plan, state, last, w_last, last_is_first, hp, stream=None):
 def mp_update_step(plan, state, last, w_last, last_is_first, max_norm, hp, stream=None):
     _check(lib().mp_update_step(plan, state, last, float(w_last), int(bool(last_is_first)),
                                 float(max_norm), ctypes.byref(hp), _stream(stream)))
+
+
+def mp_update_step_dw(plan, state, last, w_last, last_is_first, max_norm, hp, stream=None):
+    """w_last: the device address of one fp32 (a tensor element or an int)."""
+    _check(lib().mp_update_step_dw(plan, state, last, _addr(w_last), int(bool(last_is_first)),
+                                   float(max_norm), ctypes.byref(hp), _stream(stream)))
 
 
 def mp_scaler_update(state, stream=None):

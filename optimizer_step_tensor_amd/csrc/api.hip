@@ -35,7 +35,7 @@ struct mp_plan {
     bool norm_pending;
     const mp_state* norm_state;
     const mp_gradset* norm_last;
-    float norm_w_last;
+    mpk::Weight norm_w_last;
     int32_t norm_last_is_first;
     std::vector<int64_t> numel;  // per tensor, for validating FP8 output sets
 };
@@ -215,19 +215,48 @@ mp_status check_devices(const mp_plan* plan, const mp_state* state)
     return st;
 }
 
-mp_status check_last(const mp_plan* plan, const mp_gradset* last, float w_last,
+mp_status check_weight(mpk::Weight w, const char* name)
+{
+    if (w.ptr != nullptr) {
+        if ((reinterpret_cast<uintptr_t>(w.ptr) & 3u) != 0)
+            return fail(MP_ERR_ALIGN, "%s must be a 4-byte aligned device pointer", name);
+        return MP_OK;          // the value is the device's: a bad one makes the step overflow
+    }
+    if (!std::isfinite(w.value) || !(w.value > 0.0f))
+        return fail(MP_ERR_INVALID, "%s must be finite and > 0", name);
+    return MP_OK;
+}
+
+mp_status check_last(const mp_plan* plan, const mp_gradset* last, mpk::Weight w_last,
                      int32_t last_is_first)
 {
     if (last != nullptr && last->plan != plan)
         return fail(MP_ERR_INVALID, "gradset belongs to another plan");
-    if (last != nullptr && (!std::isfinite(w_last) || !(w_last > 0.0f)))
-        return fail(MP_ERR_INVALID, "w_last must be finite and > 0");
+    if (last != nullptr) {
+        mp_status st = check_weight(w_last, "w_last");
+        if (st != MP_OK) return st;
+    }
     if (last == nullptr && last_is_first)
         return fail(MP_ERR_INVALID, "last_is_first needs a gradset");
     if (grad_mode(last, last_is_first) != mpk::kLastOnly && !plan->has_acc)
         return fail(MP_ERR_INVALID, "the plan has no accumulators: pass the only micro-batch "
                                     "as `last` with last_is_first = 1");
     return MP_OK;
+}
+
+bool same_weight(mpk::Weight a, mpk::Weight b)
+{
+    return a.ptr == b.ptr && (a.ptr != nullptr || a.value == b.value);
+}
+
+mpk::Weight host_weight(float w)
+{
+    return mpk::Weight{w, nullptr};
+}
+
+mpk::Weight device_weight(const float* w)
+{
+    return mpk::Weight{0.0f, w};
 }
 
 }  // namespace
@@ -659,14 +688,16 @@ mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale)
     return ok();
 }
 
-mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
-                        mp_stream stream)
+namespace {
+
+mp_status accumulate(mp_plan* plan, const mp_gradset* g16, mpk::Weight weight, int32_t first,
+                     mp_stream stream)
 {
     if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and gradset are required");
     if (g16->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
     if (!plan->has_acc) return fail(MP_ERR_INVALID, "the plan has no accumulators");
-    if (!std::isfinite(weight) || !(weight > 0.0f)) return fail(MP_ERR_INVALID, "weight must be finite and > 0");
-    mp_status st = check_devices(plan, nullptr);
+    mp_status st = check_weight(weight, "weight");
+    if (st == MP_OK) st = check_devices(plan, nullptr);
     if (st != MP_OK) return st;
     hipError_t e = mpk::launch_accumulate(view(plan), plan->grid, g16->d_ptrs, weight, first != 0,
                                           plan->dtype, static_cast<hipStream_t>(stream));
@@ -677,9 +708,9 @@ mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int3
     return ok();
 }
 
-mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
-                                float w_last, int32_t last_is_first, float max_norm,
-                                mp_stream stream)
+mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                             mpk::Weight w_last, int32_t last_is_first, float max_norm,
+                             mp_stream stream)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     mp_status st = check_last(plan, last, w_last, last_is_first);
@@ -701,17 +732,54 @@ mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset
     return ok();
 }
 
+}  // namespace
+
+mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
+                        mp_stream stream)
+{
+    return accumulate(plan, g16, host_weight(weight), first, stream);
+}
+
+mp_status mp_accumulate_dw(mp_plan* plan, const mp_gradset* g16, const float* weight,
+                           int32_t first, mp_stream stream)
+{
+    if (weight == nullptr) return fail(MP_ERR_INVALID, "weight is NULL");
+    return accumulate(plan, g16, device_weight(weight), first, stream);
+}
+
+mp_status mp_token_weights_dev(int32_t k, const int64_t* counts, float* weights_out,
+                               mp_stream stream)
+{
+    if (k < 1 || counts == nullptr || weights_out == nullptr)
+        return fail(MP_ERR_INVALID, "need k >= 1, device counts and a device output array");
+    if ((reinterpret_cast<uintptr_t>(counts) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(weights_out) & 3u) != 0)
+        return fail(MP_ERR_ALIGN, "counts must be 8-byte aligned, weights 4-byte aligned");
+    hipError_t e = mpk::launch_token_weights(counts, k, weights_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "token weights launch");
+    return ok();
+}
+
+mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                                float w_last, int32_t last_is_first, float max_norm,
+                                mp_stream stream)
+{
+    return unscale_check_norm(plan, state, last, host_weight(w_last), last_is_first, max_norm,
+                              stream);
+}
+
 mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
                           int32_t last_is_first, double* partial_out, mp_stream stream)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     if (partial_out == nullptr || (reinterpret_cast<uintptr_t>(partial_out) & 7u) != 0)
         return fail(MP_ERR_INVALID, "partial_out must be an 8-byte aligned device pointer");
-    mp_status st = check_last(plan, last, w_last, last_is_first);
+    const mpk::Weight wl = host_weight(w_last);
+    mp_status st = check_last(plan, last, wl, last_is_first);
     if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
     hipError_t e = mpk::launch_norm_partial(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr,
-                                            w_last, grad_mode(last, last_is_first), plan->dtype,
+                                            wl, grad_mode(last, last_is_first), plan->dtype,
                                             plan->d_partials, state->d, partial_out,
                                             static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm partial launch");
@@ -719,7 +787,7 @@ mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last
     plan->norm_pending = false;
     plan->norm_state = state;
     plan->norm_last = last;
-    plan->norm_w_last = w_last;
+    plan->norm_w_last = wl;
     plan->norm_last_is_first = last_is_first ? 1 : 0;
     return ok();
 }
@@ -747,7 +815,7 @@ mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, fl
 
 namespace {
 
-mp_status adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+mp_status adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, mpk::Weight w_last,
                      int32_t last_is_first, const mp_adamw_hparams* hp, const Fp8Out* fp8,
                      mp_stream stream)
 {
@@ -757,7 +825,7 @@ mp_status adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, flo
     st = check_last(plan, last, w_last, last_is_first);
     if (st != MP_OK) return st;
     if (!plan->norm_pending || plan->norm_state != state || plan->norm_last != last ||
-        (last != nullptr && (plan->norm_w_last != w_last ||
+        (last != nullptr && (!same_weight(plan->norm_w_last, w_last) ||
                              plan->norm_last_is_first != (last_is_first ? 1 : 0))))
         return fail(MP_ERR_ORDER, "the AdamW step must follow mp_unscale_check_norm on the same "
                                   "plan and state, with the same last micro-batch arguments");
@@ -772,26 +840,9 @@ mp_status adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, flo
     return ok();
 }
 
-}  // namespace
-
-mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
-                        int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
-{
-    return adamw_step(plan, state, last, w_last, last_is_first, hp, nullptr, stream);
-}
-
-mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
-                            int32_t last_is_first, const mp_adamw_hparams* hp,
-                            const mp_fp8set* fp8, mp_stream stream)
-{
-    if (fp8 == nullptr) return fail(MP_ERR_INVALID, "fp8 set is NULL");
-    if (fp8->plan != plan) return fail(MP_ERR_INVALID, "fp8 set belongs to another plan");
-    return adamw_step(plan, state, last, w_last, last_is_first, hp, fp8->d_out, stream);
-}
-
-mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
-                         int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
-                         mp_stream stream)
+mp_status update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, mpk::Weight w_last,
+                      int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
+                      mp_stream stream)
 {
     // every structural check first, so that an error enqueues nothing
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
@@ -801,10 +852,44 @@ mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last,
         st = fail(MP_ERR_INVALID, "max_norm must be finite");
     if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
-    st = mp_unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream);
+    st = unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream);
     if (st == MP_OK) st = adamw_step(plan, state, last, w_last, last_is_first, hp, nullptr, stream);
     if (st == MP_OK) st = mp_scaler_update(state, stream);
     return st;
+}
+
+}  // namespace
+
+mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                        int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
+{
+    return adamw_step(plan, state, last, host_weight(w_last), last_is_first, hp, nullptr, stream);
+}
+
+mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                            int32_t last_is_first, const mp_adamw_hparams* hp,
+                            const mp_fp8set* fp8, mp_stream stream)
+{
+    if (fp8 == nullptr) return fail(MP_ERR_INVALID, "fp8 set is NULL");
+    if (fp8->plan != plan) return fail(MP_ERR_INVALID, "fp8 set belongs to another plan");
+    return adamw_step(plan, state, last, host_weight(w_last), last_is_first, hp, fp8->d_out,
+                      stream);
+}
+
+mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                         int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
+                         mp_stream stream)
+{
+    return update_step(plan, state, last, host_weight(w_last), last_is_first, max_norm, hp, stream);
+}
+
+mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                            const float* w_last, int32_t last_is_first, float max_norm,
+                            const mp_adamw_hparams* hp, mp_stream stream)
+{
+    if (last != nullptr && w_last == nullptr) return fail(MP_ERR_INVALID, "w_last is NULL");
+    return update_step(plan, state, last, device_weight(w_last), last_is_first, max_norm, hp,
+                       stream);
 }
 
 mp_status mp_scaler_update(mp_state* state, mp_stream stream)

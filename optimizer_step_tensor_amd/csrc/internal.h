@@ -96,6 +96,15 @@ struct AdamArgs {
     float lr, beta1, beta2, eps, weight_decay;
 };
 
+// A micro-batch weight n_i/N: a value passed with the launch or, when ptr is
+// set, one read from device memory by every block -- so that target counts
+// counted on the device need no host round trip, and a captured graph reads
+// each replay's weight.
+struct Weight {
+    float value;
+    const float* ptr;
+};
+
 // FP8 (E4M3) outputs of one tensor for the fused AdamW pass: numel codes and
 // numel/16 block scales, or both NULL (the tensor is not cast).
 struct Fp8Out {
@@ -106,19 +115,20 @@ struct Fp8Out {
 // How the gradient of one element is formed (see mp_unscale_check_norm).
 enum GradMode { kAccOnly = 0, kLastOnly = 1, kAccPlusLast = 2 };
 
-hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, float w,
+hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, Weight w,
                              int first, int dtype, hipStream_t s);
-hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
                        int mode, int dtype, double* partials, float max_norm, DevState* st,
                        hipStream_t s);
 hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* const* last,
-                               float w_last, int mode, int dtype, double* partials,
+                               Weight w_last, int mode, int dtype, double* partials,
                                const DevState* st, double* out, hipStream_t s);
 hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s);
-hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
                         int mode, int dtype, const AdamArgs& a, const Fp8Out* fp8, DevState* st,
                         hipStream_t s);
 hipError_t launch_scaler(DevState* st, hipStream_t s);
+hipError_t launch_token_weights(const int64_t* counts, int k, float* weights, hipStream_t s);
 hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s);
 hipError_t launch_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n, int block,
                              hipStream_t s);

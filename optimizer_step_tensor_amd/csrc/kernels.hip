@@ -187,6 +187,11 @@ __device__ __forceinline__ int valid_count(int len, int e)
     return r > kGroup ? kGroup : r;
 }
 
+__device__ __forceinline__ float weight_of(const Weight& w)
+{
+    return w.ptr != nullptr ? *w.ptr : w.value;
+}
+
 // The fp32 gradient of one element ("Megatron Internals III", section 8;
 // "Mixed precision ...", section 2 "Gradient accumulation"): the accumulated
 // buffer, the last micro-batch alone, or the last micro-batch added to the
@@ -223,8 +228,9 @@ __device__ __forceinline__ double block_sum(double x)
 template <int DT, bool FIRST>
 __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
                                                        const uint16_t* const* __restrict__ g16,
-                                                       float w)
+                                                       Weight wt)
 {
+    const float w = weight_of(wt);
     for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
          c += gridDim.x) {
         const Chunk ch = p.chunks[c];
@@ -265,10 +271,11 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
 template <int DT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
                                                          const uint16_t* const* __restrict__ last,
-                                                         float w_last,
+                                                         Weight wl,
                                                          const DevState* __restrict__ st,
                                                          double* __restrict__ partials)
 {
+    const float w_last = weight_of(wl);
     const float inv = st->inv_scale;
     double s = 0.0;
     for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
@@ -451,11 +458,12 @@ __device__ __forceinline__ void store_scale(float* p, float scale)
 template <int DT, int MODE, bool FP8>
 __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
                                                   const uint16_t* const* __restrict__ last,
-                                                  float w_last, AdamArgs a,
+                                                  Weight wl, AdamArgs a,
                                                   const Fp8Out* __restrict__ fp8,
                                                   const DevState* __restrict__ st)
 {
     if (st->s.found_inf) return;                  // skipped step: write nothing
+    const float w_last = weight_of(wl);
     const float scale = st->update_scale;
     const float bc1 = static_cast<float>(1.0 - st->s.beta1_pow * static_cast<double>(a.beta1));
     const float bc2 = static_cast<float>(1.0 - st->s.beta2_pow * static_cast<double>(a.beta2));
@@ -573,6 +581,37 @@ __global__ void k_scaler(DevState* __restrict__ st)
     st->inv_scale = 1.0f / scale;
 }
 
+// Token weights on the device ("Accumulate gradients and recompute activations",
+// "Weight each mean by the targets it represents"): w_i = fp32(n_i / N) with
+// N = sum of the counts, in binary64 then rounded once -- the host helper's
+// arithmetic.  Counts the host helper would refuse (n_i <= 0, N > 2^53) give NaN
+// weights, so that the step they feed overflows and is skipped.
+__global__ __launch_bounds__(kBlock) void k_token_weights(const int64_t* __restrict__ counts, int k,
+                                                          float* __restrict__ weights)
+{
+    __shared__ double total;
+    __shared__ int valid;
+    if (threadIdx.x == 0) {
+        const int64_t limit = int64_t(1) << 53;
+        int64_t n = 0;
+        int ok = 1;
+        for (int i = 0; i < k; ++i) {              // in order, stopping the sum at the limit
+            const int64_t c = counts[i];
+            if (c <= 0 || c > limit - n) {
+                ok = 0;
+                break;
+            }
+            n += c;
+        }
+        total = static_cast<double>(n);
+        valid = ok;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < k; i += kBlock)
+        weights[i] = valid ? static_cast<float>(static_cast<double>(counts[i]) / total)
+                           : __builtin_nanf("");
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_cast_to_16(const float* __restrict__ src,
                                                        uint16_t* __restrict__ dst, int64_t n)
@@ -672,14 +711,14 @@ unsigned elementwise_grid(int64_t n)
 }
 
 template <int DT, int MODE>
-void launch_norm_t(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+void launch_norm_t(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
                    double* partials, DevState* st, hipStream_t s)
 {
     k_norm_partial<DT, MODE><<<grid, kBlock, 0, s>>>(p, last, w_last, st, partials);
 }
 
 template <int DT, int MODE>
-void launch_adamw_t(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+void launch_adamw_t(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
                     const AdamArgs& a, const Fp8Out* fp8, DevState* st, hipStream_t s)
 {
     if (fp8 != nullptr) k_adamw<DT, MODE, true><<<grid, kBlock, 0, s>>>(p, last, w_last, a, fp8, st);
@@ -688,7 +727,7 @@ void launch_adamw_t(const PlanView& p, int grid, const uint16_t* const* last, fl
 
 }  // namespace
 
-hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, float w,
+hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, Weight w,
                              int first, int dtype, hipStream_t s)
 {
     if (dtype == MP_BF16) {
@@ -701,7 +740,7 @@ hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const*
     return hipGetLastError();
 }
 
-hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
                        int mode, int dtype, double* partials, float max_norm, DevState* st,
                        hipStream_t s)
 {
@@ -723,7 +762,7 @@ hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last,
 }
 
 hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* const* last,
-                               float w_last, int mode, int dtype, double* partials,
+                               Weight w_last, int mode, int dtype, double* partials,
                                const DevState* st, double* out, hipStream_t s)
 {
     DevState* stm = const_cast<DevState*>(st);
@@ -750,7 +789,7 @@ hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, 
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, float w_last,
+hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
                         int mode, int dtype, const AdamArgs& a, const Fp8Out* fp8, DevState* st,
                         hipStream_t s)
 {
@@ -772,6 +811,12 @@ hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last
 hipError_t launch_scaler(DevState* st, hipStream_t s)
 {
     k_scaler<<<1, 64, 0, s>>>(st);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_weights(const int64_t* counts, int k, float* weights, hipStream_t s)
+{
+    k_token_weights<<<1, kBlock, 0, s>>>(counts, k, weights);
     return hipGetLastError();
 }
 

@@ -96,6 +96,9 @@ class DeviceRun:
         self.fp8set = None                 # set: steps use the fused AdamW + FP8 entry point
         self.one_call = False              # True: steps use mp_update_step
         self.fold_last = True              # False: accumulate every micro-batch, then norm/AdamW
+        self.device_weights = False        # True: weights from device counts, steps use the
+        self.dev_counts = None             # *_dw entry points (kept alive until the next step)
+        self.dev_weights = None
 
     def stats(self):
         return self.mp.read_stats(self.state)
@@ -118,6 +121,8 @@ class DeviceRun:
         mp, w, s = self.mp, self.w, self.step_no
         assert len(self.g16) == w.k, "per-micro-batch buffers needed to run a step"
         self.fill_grads(s, scale)
+        if self.device_weights:
+            return self._step_device_weights(s, snapshot)
         weights = mp.mp_token_weights(w.token_counts(s))
         if not self.fold_last:
             for i in range(w.k):
@@ -143,6 +148,26 @@ class DeviceRun:
             mp.mp_adamw_step_fp8(self.model.plan, self.state, last, weights[-1], lif, self.hp,
                                  self.fp8set)
         mp.mp_scaler_update(self.state)
+        return acc_snapshot
+
+    def _step_device_weights(self, s, snapshot):
+        """The step with n_i in device memory: mp_token_weights_dev, mp_accumulate_dw and
+        mp_update_step_dw read the weights where the kernels run."""
+        torch, mp, w = self.torch, self.mp, self.w
+        self.dev_counts = torch.tensor(w.token_counts(s), dtype=torch.int64, device="cuda")
+        self.dev_weights = torch.empty(w.k, dtype=torch.float32, device="cuda")
+        mp.mp_token_weights_dev(w.k, self.dev_counts, self.dev_weights)
+        wp = [self.dev_weights.data_ptr() + 4 * i for i in range(w.k)]
+        n_acc = w.k if not self.fold_last else w.k - 1
+        for i in range(n_acc):
+            mp.mp_accumulate_dw(self.model.plan, self.gsets[i], wp[i], i == 0)
+        acc_snapshot = ([a.cpu().numpy() for a in self.model.acc]
+                        if snapshot and self.model.acc is not None else None)
+        if not self.fold_last:
+            mp.mp_update_step_dw(self.model.plan, self.state, None, None, 0, w.max_norm, self.hp)
+        else:
+            mp.mp_update_step_dw(self.model.plan, self.state, self.gsets[w.k - 1], wp[-1],
+                                 w.k == 1, w.max_norm, self.hp)
         return acc_snapshot
 
     def host(self, name):

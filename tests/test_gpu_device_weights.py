@@ -1,0 +1,175 @@
+"""Token weights computed and read on the device (needs an MI355X).
+
+The weights of "Accumulate gradients and recompute activations", section "Weight each mean by
+the targets it represents", from counts that stay in device memory: mp_token_weights_dev must
+give the host call's bits, the *_dw entry points must step exactly as the host-weight ones do,
+counts the host would refuse must turn into a skipped step, and a captured graph must read the
+counts of each replay.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from inputs import configs  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mp():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import optimizer_step_tensor_amd as m
+    m.lib()
+    return m
+
+
+def device_weights(mp, counts):
+    import torch
+    c = torch.tensor(counts, dtype=torch.int64, device="cuda")
+    w = torch.full((len(counts),), 7.0, dtype=torch.float32, device="cuda")
+    mp.mp_token_weights_dev(len(counts), c, w)
+    return w.cpu().numpy()
+
+
+def test_device_weights_equal_the_oracle(mp):
+    """fp32(n_i / N) bit for bit, for k up to beyond one block of threads and totals up to 2^53."""
+    rng = np.random.default_rng(44)
+    cases = [list(rng.integers(1, 10 ** 6, k)) for k in (1, 2, 3, 4, 8, 31, 256, 257, 1000)]
+    cases += [[2 ** 52, 2 ** 52], [2 ** 53 - 1, 1], [1] * 3, [3, 2 ** 40, 7]]
+    for counts in cases:
+        got = device_weights(mp, counts)
+        ref = oracle.token_weights(counts)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), counts[:4]
+        assert np.array_equal(got, np.array(mp.mp_token_weights(counts), np.float32))
+
+
+def test_refused_counts_give_nan_weights(mp):
+    """Counts the host call refuses (a micro-batch without targets, N > 2^53) cannot be refused
+    on the device without a sync: every weight comes out NaN instead."""
+    for counts in ([4, 0], [0], [-3, 5, 6], [2 ** 53, 1], [2 ** 62, 2 ** 62, 1], [1, 2, -(2 ** 63)]):
+        with pytest.raises(ValueError):
+            oracle.token_weights(counts)
+        got = device_weights(mp, counts)
+        assert np.isnan(got).all(), counts
+
+
+@pytest.mark.parametrize("name,fold_last", [("edges-fp16", True), ("llama-10.5M", True),
+                                            ("edges", False)])
+def test_device_weight_steps_equal_the_oracle(mp, name, fold_last):
+    """Steps driven by mp_token_weights_dev, mp_accumulate_dw and mp_update_step_dw equal the
+    oracle's, through the fp16 list's overflow and change of S."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make(name)
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    orc.fold_last = dev.fold_last = fold_last
+    dev.device_weights = True
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            say("  step", s, compare_step(dev, orc, w, s))
+    finally:
+        dev.close()
+
+
+def test_refused_counts_skip_the_step(mp):
+    """A count of zero on the device makes the weights NaN, so the step is skipped exactly as an
+    overflow is ("Discard a failed partial logical update"): no master, moment or 16-bit weight
+    changes, the clock stays, and the scaler backs off."""
+    import torch
+    from harness import DeviceRun
+    w = configs.make("edges-fp16")
+    dev = DeviceRun(w)
+    dev.device_weights = True
+    try:
+        dev.step(w.scaler["init_scale"])
+        before = dev.stats()
+        assert before["skipped"] == 0
+        snap = {n: [x.clone() for x in getattr(dev.model, n)] for n in ("master", "m", "v", "w16")}
+        dev.fill_grads(2, before["scale"])
+        cnt = torch.tensor([0] + [5] * (w.k - 1), dtype=torch.int64, device="cuda")
+        wts = torch.empty(w.k, dtype=torch.float32, device="cuda")
+        mp.mp_token_weights_dev(w.k, cnt, wts)
+        plan = dev.model.plan
+        for i in range(w.k - 1):
+            mp.mp_accumulate_dw(plan, dev.gsets[i], wts.data_ptr() + 4 * i, i == 0)
+        mp.mp_update_step_dw(plan, dev.state, dev.gsets[-1], wts.data_ptr() + 4 * (w.k - 1),
+                             w.k == 1, w.max_norm, dev.hp)
+        after = dev.stats()
+        say("  after refused counts:", after)
+        assert after["found_inf"] == 1 and after["skipped"] == 1
+        assert after["step"] == before["step"]
+        assert after["skipped_total"] == before["skipped_total"] + 1
+        assert after["good_steps"] == 0
+        assert after["scale"] == max(before["scale"] * w.scaler["backoff"], w.scaler["min_scale"])
+        assert after["beta1_pow"] == before["beta1_pow"]
+        for n, xs in snap.items():
+            for x, y in zip(xs, getattr(dev.model, n)):
+                assert torch.equal(x.view(torch.int16 if n == "w16" else torch.int32),
+                                   y.view(torch.int16 if n == "w16" else torch.int32)), n
+    finally:
+        dev.close()
+
+
+def test_graph_replays_read_each_replays_counts(mp):
+    """A captured step (device weights, accumulation, update) replayed with new counts written
+    into the same device buffer between replays equals eager steps with host weights of those
+    counts, bit for bit, on every replay."""
+    import torch
+    from harness import DeviceRun
+    w = configs.make("llama-10.5M")
+    eager, graphed = DeviceRun(w), DeviceRun(w)
+    k = w.k
+    cnt = torch.ones(k, dtype=torch.int64, device="cuda")
+    wts = torch.empty(k, dtype=torch.float32, device="cuda")
+    wp = [wts.data_ptr() + 4 * i for i in range(k)]
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        st = torch.cuda.current_stream()
+        plan = graphed.model.plan
+        mp.mp_token_weights_dev(k, cnt, wts, st)
+        for i in range(k - 1):
+            mp.mp_accumulate_dw(plan, graphed.gsets[i], wp[i], i == 0, st)
+        mp.mp_update_step_dw(plan, graphed.state, graphed.gsets[-1], wp[-1], 0, w.max_norm,
+                             graphed.hp, st)
+    try:
+        for r in range(1, 5):
+            counts = w.token_counts(r)
+            eager.fill_grads(r, 1.0)
+            graphed.fill_grads(r, 1.0)
+            cnt.copy_(torch.tensor(counts, dtype=torch.int64))
+            torch.cuda.synchronize()
+            weights = mp.mp_token_weights(counts)
+            plan = eager.model.plan
+            for i in range(k - 1):
+                mp.mp_accumulate(plan, eager.gsets[i], weights[i], i == 0)
+            mp.mp_update_step(plan, eager.state, eager.gsets[-1], weights[-1], 0, w.max_norm,
+                              eager.hp)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(wts.cpu().numpy(), np.array(weights, np.float32)), r
+            a, b = eager.stats(), graphed.stats()
+            assert a == b and a["step"] == r
+            for name in ("acc", "master", "m", "v"):
+                for x, y in zip(getattr(eager.model, name), getattr(graphed.model, name)):
+                    assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (r, name)
+            for x, y in zip(eager.model.w16, graphed.model.w16):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (r, "w16")
+            say("  replay", r, "counts", counts)
+    finally:
+        del g
+        eager.close()
+        graphed.close()

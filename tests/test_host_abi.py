@@ -159,6 +159,17 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_update_step(None, None, None, 1.0, 0, 1.0, None, None) == mp.MP_ERR_INVALID
     assert (L.mp_norm_partial(fake_state, fake_state, None, 1.0, 0, ctypes.c_void_p(0x10001), None)
             == mp.MP_ERR_INVALID)
+    # device-weight entry points: NULL, k and alignment checks come before any launch
+    dev = ctypes.c_void_p(0x10000)
+    assert L.mp_token_weights_dev(0, dev, dev, None) == mp.MP_ERR_INVALID
+    assert L.mp_token_weights_dev(2, None, dev, None) == mp.MP_ERR_INVALID
+    assert L.mp_token_weights_dev(2, ctypes.c_void_p(0x10004), dev, None) == mp.MP_ERR_ALIGN
+    assert L.mp_token_weights_dev(2, dev, ctypes.c_void_p(0x10002), None) == mp.MP_ERR_ALIGN
+    assert L.mp_accumulate_dw(None, None, dev, 1, None) == mp.MP_ERR_INVALID
+    assert L.mp_accumulate_dw(fake_state, fake_state, None, 1, None) == mp.MP_ERR_INVALID
+    assert L.mp_update_step_dw(None, None, None, dev, 0, 1.0, None, None) == mp.MP_ERR_INVALID
+    assert (L.mp_update_step_dw(fake_state, fake_state, fake_state, None, 0, 1.0, None, None)
+            == mp.MP_ERR_INVALID)
 
 
 def test_bench_refuses_more_than_one_gpu():
