@@ -211,7 +211,11 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
       timed the same way in alternation;
     - saving and restoring the device state (scaler and optimizer clock);
     - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
-      multiples of 64 elements), its accumulate passes, partial norm + finish, AdamW, scaler."""
+      multiples of 64 elements), its accumulate passes, partial norm + finish, AdamW, scaler;
+    - the step with k <= 4 micro-batch gradients resident, folded in groups: two accumulated in
+      one pass and two folded into the norm and AdamW passes, or all k folded there (no
+      accumulator pass at all).  Same results, bit for bit, as the timed step."""
+    sets_main = sets
     out = {}
     P, k = w.total, w.k
     # context for the roofline: the runtime's own device-to-device copy of 4 GiB
@@ -276,6 +280,43 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
         mp.mp_gradset_destroy(g)
     mp.mp_state_destroy(st)
     mp.mp_plan_destroy(plan)
+    if 2 <= k <= 4:
+        out["resident_groups"] = time_groups(mp, torch, w, model, sets_main, state, hp, weights,
+                                             stream)
+    return out
+
+
+def group_bytes_per_param(acc_groups, fold):
+    """Algorithmic bytes per parameter of one step folded in groups: an accumulate pass of n
+    micro-batches reads 2n (+4 for the accumulator unless it is the first) and writes 4; the
+    norm reads 2n (+4) and AdamW 2n (+4) + 12 and writes 14, the +4 when the step has an
+    accumulator."""
+    b = sum(2 * len(g) + (4 if i == 0 else 8) for i, g in enumerate(acc_groups))
+    acc = 4 if acc_groups else 0
+    return b + (acc + 2 * len(fold)) + (acc + 2 * len(fold) + 12 + 14)
+
+
+def time_groups(mp, torch, w, model, sets, state, hp, weights, stream, reps=3):
+    k = w.k
+    schedules = {"all_folded": ([], list(range(k)))}
+    if k >= 3:
+        schedules["two_accumulated"] = ([[0, 1]], list(range(2, k)))
+    out = {}
+    for name, (acc_groups, fold) in schedules.items():
+        def step():
+            for i, g in enumerate(acc_groups):
+                mp.mp_accumulate_group(model.plan, [sets[j] for j in g], [weights[j] for j in g],
+                                       i == 0, stream)
+            mp.mp_update_step_group(model.plan, state, [sets[j] for j in fold],
+                                    [weights[j] for j in fold], not acc_groups, w.max_norm, hp,
+                                    stream)
+        ms = time_launches(torch, stream, step, reps)
+        bpp = group_bytes_per_param(acc_groups, fold)
+        out[name] = {"schedule": {"accumulated": acc_groups, "folded": fold},
+                     "bytes_per_param": bpp, "ms_per_step": ms,
+                     "params_per_s": w.total / (ms * 1e-3),
+                     "GBps": bpp * w.total / ms / 1e6,
+                     "frac": bpp * w.total / ms / 1e6 / HBM_PEAK_GBPS}
     return out
 
 

@@ -252,6 +252,24 @@ mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int3
 mp_status mp_accumulate_dw(mp_plan* plan, const mp_gradset* g16, const float* weight,
                            int32_t first, mp_stream stream);
 
+/* Accumulate n resident micro-batches (1 <= n <= 4) in one pass, for a caller
+ * that keeps several micro-batch gradients in device memory at once.  The
+ * result is bit for bit that of n mp_accumulate calls in array order (the
+ * first with `first`, the rest with first = 0), since every term is added with
+ * the same two roundings, in the same order, while the running sum stays in a
+ * register.  The accumulator is read once (not at all when first != 0) and
+ * written once, so the pass moves 2n + 8 bytes per parameter (2n + 4 when
+ * first) instead of 10n (10n - 4).
+ *   sets:    n gradsets of this plan, in micro-batch order (host array);
+ *   weights: n weights, a host array, or when weights_on_device != 0 a device
+ *            array of n fp32 (4-byte aligned, e.g. part of the output of
+ *            mp_token_weights_dev), read when the kernel runs.
+ * MP_ERR_INVALID if n is out of range, an argument is NULL, a gradset belongs
+ * to another plan or the plan has no accumulators. */
+mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, const float* weights,
+                              int32_t n, int32_t weights_on_device, int32_t first,
+                              mp_stream stream);
+
 /* Unscale, check and measure ("Megatron Internals III", sections 4, 6 and 9;
  * "Mixed precision ...", section 2 "Dynamic scaling").  The gradient of each
  * element is g_eff = acc (last == NULL), fl(w_last * widen(last))
@@ -331,6 +349,22 @@ mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last,
 mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* last,
                             const float* w_last, int32_t last_is_first, float max_norm,
                             const mp_adamw_hparams* hp, mp_stream stream);
+
+/* mp_update_step with the last n micro-batches (1 <= n <= 4) resident and all
+ * folded into the norm pass and the AdamW pass, as `last` is folded in for
+ * n = 1.  The gradient of each element is the accumulator (skipped when
+ * last_is_first != 0, so that with k <= 4 micro-batches no accumulator is
+ * needed at all) followed by the n terms in array order, each added with the
+ * roundings of mp_accumulate: bit for bit the gradient mp_update_step sees
+ * after accumulating all but the last micro-batch one by one.  Per parameter,
+ * the norm pass reads 4 + 2n bytes (2n with last_is_first) and AdamW 30 + 2n
+ * (26 + 2n) bytes, so k = 4 micro-batches cost 42 bytes in all, against 64 for
+ * the one-at-a-time schedule.  sets and weights as in mp_accumulate_group.
+ * Same checks, order and results as mp_update_step. */
+mp_status mp_update_step_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,
+                               const float* weights, int32_t n, int32_t weights_on_device,
+                               int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
+                               mp_stream stream);
 
 /* Elementwise casts with the step's conversions: dst = round-to-nearest-even
  * of src into the 16-bit format (as in mp_adamw_step), and dst = exact fp32

@@ -32,7 +32,7 @@ ENTRY_POINTS = [
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
     "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_dw",
-    "mp_update_step_dw",
+    "mp_update_step_dw", "mp_accumulate_group", "mp_update_step_group",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -122,6 +122,9 @@ def _bind(L):
         "mp_token_weights_dev": ([i32, P, P, P], i32),
         "mp_accumulate_dw": ([P, P, P, i32, P], i32),
         "mp_update_step_dw": ([P, P, P, P, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
+        "mp_accumulate_group": ([P, PP, P, i32, i32, i32, P], i32),
+        "mp_update_step_group": ([P, P, PP, P, i32, i32, i32, f32, ctypes.POINTER(AdamWHparams),
+                                  P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -278,6 +281,24 @@ def mp_accumulate_dw(plan, gradset, weight, first, stream=None):
                                   _stream(stream)))
 
 
+def _group(sets, weights):
+    """(gradset array, weight pointer, on_device) for the *_group entry points: weights is a
+    list of floats, or a device fp32 tensor (or a device address) holding len(sets) weights."""
+    arr = (ctypes.c_void_p * len(sets))(*[s.value if isinstance(s, ctypes.c_void_p) else s
+                                          for s in sets])
+    if isinstance(weights, (torch.Tensor, int)):
+        return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), _addr(weights), 1
+    w = (ctypes.c_float * len(sets))(*[float(x) for x in weights])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), ctypes.cast(w, ctypes.c_void_p), 0
+
+
+def mp_accumulate_group(plan, sets, weights, first, stream=None):
+    """Accumulate len(sets) resident micro-batches in one pass (see mp_accumulate_group)."""
+    arr, w, dev = _group(sets, weights)
+    _check(lib().mp_accumulate_group(plan, arr, w, len(sets), dev, int(bool(first)),
+                                     _stream(stream)))
+
+
 def mp_unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream=None):
     _check(lib().mp_unscale_check_norm(plan, state, last, float(w_last), int(bool(last_is_first)),
                                        float(max_norm), _stream(stream)))
@@ -297,6 +318,14 @@ def mp_update_step_dw(plan, state, last, w_last, last_is_first, max_norm, hp, st
     """w_last: the device address of one fp32 (a tensor element or an int)."""
     _check(lib().mp_update_step_dw(plan, state, last, _addr(w_last), int(bool(last_is_first)),
                                    float(max_norm), ctypes.byref(hp), _stream(stream)))
+
+
+def mp_update_step_group(plan, state, sets, weights, last_is_first, max_norm, hp, stream=None):
+    """mp_update_step with len(sets) resident micro-batches folded in (see the header)."""
+    arr, w, dev = _group(sets, weights)
+    _check(lib().mp_update_step_group(plan, state, arr, w, len(sets), dev,
+                                      int(bool(last_is_first)), float(max_norm),
+                                      ctypes.byref(hp), _stream(stream)))
 
 
 def mp_scaler_update(state, stream=None):

@@ -16,6 +16,16 @@ using mpk::DevState;
 using mpk::Fp8Out;
 using mpk::TensorDesc;
 
+// The micro-batches one pass folds in after the accumulator, in order: the
+// host view of mpk::Grads.  no_acc: the group starts the update (no
+// accumulator term).
+struct Group {
+    const mp_gradset* sets[mpk::kMaxGroup];
+    mpk::Weight w[mpk::kMaxGroup];
+    int32_t n;
+    int32_t no_acc;
+};
+
 struct mp_plan {
     int device;
     int32_t n_tensors;
@@ -34,9 +44,7 @@ struct mp_plan {
     bool partial_pending;
     bool norm_pending;
     const mp_state* norm_state;
-    const mp_gradset* norm_last;
-    mpk::Weight norm_w_last;
-    int32_t norm_last_is_first;
+    Group norm_group;         // the micro-batches the pending norm folded in
     std::vector<int64_t> numel;  // per tensor, for validating FP8 output sets
 };
 
@@ -189,11 +197,6 @@ mp_status check_hparams(const mp_adamw_hparams* hp)
     return MP_OK;
 }
 
-int grad_mode(const mp_gradset* last, int32_t last_is_first)
-{
-    if (last == nullptr) return mpk::kAccOnly;
-    return last_is_first ? mpk::kLastOnly : mpk::kAccPlusLast;
-}
 
 // Plans and states are bound to the device current at their creation; a hot
 // call made with another device current would launch on the wrong GPU.
@@ -227,18 +230,19 @@ mp_status check_weight(mpk::Weight w, const char* name)
     return MP_OK;
 }
 
-mp_status check_last(const mp_plan* plan, const mp_gradset* last, mpk::Weight w_last,
-                     int32_t last_is_first)
+mp_status check_group(const mp_plan* plan, const Group& g)
 {
-    if (last != nullptr && last->plan != plan)
-        return fail(MP_ERR_INVALID, "gradset belongs to another plan");
-    if (last != nullptr) {
-        mp_status st = check_weight(w_last, "w_last");
+    if (g.n < 0 || g.n > mpk::kMaxGroup)
+        return fail(MP_ERR_INVALID, "a group holds 1 to %d gradsets", mpk::kMaxGroup);
+    for (int i = 0; i < g.n; ++i) {
+        if (g.sets[i] == nullptr) return fail(MP_ERR_INVALID, "gradset %d of the group is NULL", i);
+        if (g.sets[i]->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
+        mp_status st = check_weight(g.w[i], "a micro-batch weight");
         if (st != MP_OK) return st;
     }
-    if (last == nullptr && last_is_first)
+    if (g.n == 0 && g.no_acc)
         return fail(MP_ERR_INVALID, "last_is_first needs a gradset");
-    if (grad_mode(last, last_is_first) != mpk::kLastOnly && !plan->has_acc)
+    if (!g.no_acc && !plan->has_acc)
         return fail(MP_ERR_INVALID, "the plan has no accumulators: pass the only micro-batch "
                                     "as `last` with last_is_first = 1");
     return MP_OK;
@@ -249,6 +253,26 @@ bool same_weight(mpk::Weight a, mpk::Weight b)
     return a.ptr == b.ptr && (a.ptr != nullptr || a.value == b.value);
 }
 
+bool same_group(const Group& a, const Group& b)
+{
+    if (a.n != b.n || a.no_acc != b.no_acc) return false;
+    for (int i = 0; i < a.n; ++i)
+        if (a.sets[i] != b.sets[i] || !same_weight(a.w[i], b.w[i])) return false;
+    return true;
+}
+
+mpk::Grads device_group(const Group& g)
+{
+    mpk::Grads d{};
+    for (int i = 0; i < g.n; ++i) {
+        d.set[i] = g.sets[i]->d_ptrs;
+        d.w[i] = g.w[i];
+    }
+    d.n = g.n;
+    d.acc = g.no_acc ? 0 : 1;
+    return d;
+}
+
 mpk::Weight host_weight(float w)
 {
     return mpk::Weight{w, nullptr};
@@ -257,6 +281,37 @@ mpk::Weight host_weight(float w)
 mpk::Weight device_weight(const float* w)
 {
     return mpk::Weight{0.0f, w};
+}
+
+// The single-`last` form of the hot calls as a group of 0 or 1.
+Group single(const mp_gradset* last, mpk::Weight w_last, int32_t last_is_first)
+{
+    Group g{};
+    g.n = last != nullptr ? 1 : 0;
+    g.sets[0] = last;
+    g.w[0] = w_last;
+    g.no_acc = last_is_first ? 1 : 0;
+    return g;
+}
+
+// A caller's array of n gradsets and n weights (host floats, or a device array
+// of n floats when on_device).
+mp_status make_group(const mp_gradset* const* sets, const float* weights, int32_t n,
+                     int32_t on_device, int32_t no_acc, Group* out)
+{
+    if (n < 1 || n > mpk::kMaxGroup)
+        return fail(MP_ERR_INVALID, "a group holds 1 to %d gradsets", mpk::kMaxGroup);
+    if (sets == nullptr || weights == nullptr)
+        return fail(MP_ERR_INVALID, "sets and weights are required");
+    Group g{};
+    g.n = n;
+    g.no_acc = no_acc ? 1 : 0;
+    for (int i = 0; i < n; ++i) {
+        g.sets[i] = sets[i];
+        g.w[i] = on_device ? device_weight(weights + i) : host_weight(weights[i]);
+    }
+    *out = g;
+    return MP_OK;
 }
 
 }  // namespace
@@ -690,16 +745,17 @@ mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale)
 
 namespace {
 
-mp_status accumulate(mp_plan* plan, const mp_gradset* g16, mpk::Weight weight, int32_t first,
-                     mp_stream stream)
+mp_status accumulate(mp_plan* plan, const Group& g, int32_t first, mp_stream stream)
 {
-    if (plan == nullptr || g16 == nullptr) return fail(MP_ERR_INVALID, "plan and gradset are required");
-    if (g16->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
+    if (plan == nullptr) return fail(MP_ERR_INVALID, "plan is required");
+    if (g.n < 1) return fail(MP_ERR_INVALID, "a gradset is required");
     if (!plan->has_acc) return fail(MP_ERR_INVALID, "the plan has no accumulators");
-    mp_status st = check_weight(weight, "weight");
+    Group gg = g;
+    gg.no_acc = 1;            // the accumulator is the destination, not a term
+    mp_status st = check_group(plan, gg);
     if (st == MP_OK) st = check_devices(plan, nullptr);
     if (st != MP_OK) return st;
-    hipError_t e = mpk::launch_accumulate(view(plan), plan->grid, g16->d_ptrs, weight, first != 0,
+    hipError_t e = mpk::launch_accumulate(view(plan), plan->grid, device_group(gg), first != 0,
                                           plan->dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
     // the buffers changed: a norm measured before this no longer describes them
@@ -708,28 +764,63 @@ mp_status accumulate(mp_plan* plan, const mp_gradset* g16, mpk::Weight weight, i
     return ok();
 }
 
-mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* last,
-                             mpk::Weight w_last, int32_t last_is_first, float max_norm,
+mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, float max_norm,
                              mp_stream stream)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
-    mp_status st = check_last(plan, last, w_last, last_is_first);
+    mp_status st = check_group(plan, g);
     if (st != MP_OK) return st;
     if (std::isnan(max_norm) || std::isinf(max_norm)) return fail(MP_ERR_INVALID, "max_norm must be finite");
     st = check_devices(plan, state);
     if (st != MP_OK) return st;
-    hipError_t e = mpk::launch_norm(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr, w_last,
-                                    grad_mode(last, last_is_first), plan->dtype, plan->d_partials,
-                                    max_norm, state->d, static_cast<hipStream_t>(stream));
+    hipError_t e = mpk::launch_norm(view(plan), plan->norm_grid, device_group(g), plan->dtype,
+                                    plan->d_partials, max_norm, state->d,
+                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm launch");
     state->decision_pending = true;
     plan->partial_pending = false;
     plan->norm_pending = true;
     plan->norm_state = state;
-    plan->norm_last = last;
-    plan->norm_w_last = w_last;
-    plan->norm_last_is_first = last_is_first ? 1 : 0;
+    plan->norm_group = g;
     return ok();
+}
+
+mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_adamw_hparams* hp,
+                     const Fp8Out* fp8, mp_stream stream)
+{
+    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
+    mp_status st = check_hparams(hp);
+    if (st != MP_OK) return st;
+    st = check_group(plan, g);
+    if (st != MP_OK) return st;
+    if (!plan->norm_pending || plan->norm_state != state || !same_group(plan->norm_group, g))
+        return fail(MP_ERR_ORDER, "the AdamW step must follow mp_unscale_check_norm on the same "
+                                  "plan and state, with the same last micro-batch arguments");
+    st = check_devices(plan, state);
+    if (st != MP_OK) return st;
+    mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    hipError_t e = mpk::launch_adamw(view(plan), plan->grid, device_group(g), plan->dtype, a, fp8,
+                                     state->d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "adamw launch");
+    plan->norm_pending = false;
+    return ok();
+}
+
+mp_status update_step(mp_plan* plan, mp_state* state, const Group& g, float max_norm,
+                      const mp_adamw_hparams* hp, mp_stream stream)
+{
+    // every structural check first, so that an error enqueues nothing
+    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
+    mp_status st = check_hparams(hp);
+    if (st == MP_OK) st = check_group(plan, g);
+    if (st == MP_OK && (std::isnan(max_norm) || std::isinf(max_norm)))
+        st = fail(MP_ERR_INVALID, "max_norm must be finite");
+    if (st == MP_OK) st = check_devices(plan, state);
+    if (st != MP_OK) return st;
+    st = unscale_check_norm(plan, state, g, max_norm, stream);
+    if (st == MP_OK) st = adamw_step(plan, state, g, hp, nullptr, stream);
+    if (st == MP_OK) st = mp_scaler_update(state, stream);
+    return st;
 }
 
 }  // namespace
@@ -737,14 +828,26 @@ mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset* l
 mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
                         mp_stream stream)
 {
-    return accumulate(plan, g16, host_weight(weight), first, stream);
+    if (g16 == nullptr) return fail(MP_ERR_INVALID, "plan and gradset are required");
+    return accumulate(plan, single(g16, host_weight(weight), 1), first, stream);
 }
 
 mp_status mp_accumulate_dw(mp_plan* plan, const mp_gradset* g16, const float* weight,
                            int32_t first, mp_stream stream)
 {
     if (weight == nullptr) return fail(MP_ERR_INVALID, "weight is NULL");
-    return accumulate(plan, g16, device_weight(weight), first, stream);
+    if (g16 == nullptr) return fail(MP_ERR_INVALID, "plan and gradset are required");
+    return accumulate(plan, single(g16, device_weight(weight), 1), first, stream);
+}
+
+mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, const float* weights,
+                              int32_t n, int32_t weights_on_device, int32_t first,
+                              mp_stream stream)
+{
+    Group g;
+    mp_status st = make_group(sets, weights, n, weights_on_device, 1, &g);
+    if (st != MP_OK) return st;
+    return accumulate(plan, g, first, stream);
 }
 
 mp_status mp_token_weights_dev(int32_t k, const int64_t* counts, float* weights_out,
@@ -764,8 +867,8 @@ mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset
                                 float w_last, int32_t last_is_first, float max_norm,
                                 mp_stream stream)
 {
-    return unscale_check_norm(plan, state, last, host_weight(w_last), last_is_first, max_norm,
-                              stream);
+    return unscale_check_norm(plan, state, single(last, host_weight(w_last), last_is_first),
+                              max_norm, stream);
 }
 
 mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
@@ -774,21 +877,18 @@ mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     if (partial_out == nullptr || (reinterpret_cast<uintptr_t>(partial_out) & 7u) != 0)
         return fail(MP_ERR_INVALID, "partial_out must be an 8-byte aligned device pointer");
-    const mpk::Weight wl = host_weight(w_last);
-    mp_status st = check_last(plan, last, wl, last_is_first);
+    const Group g = single(last, host_weight(w_last), last_is_first);
+    mp_status st = check_group(plan, g);
     if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
-    hipError_t e = mpk::launch_norm_partial(view(plan), plan->norm_grid, last ? last->d_ptrs : nullptr,
-                                            wl, grad_mode(last, last_is_first), plan->dtype,
-                                            plan->d_partials, state->d, partial_out,
+    hipError_t e = mpk::launch_norm_partial(view(plan), plan->norm_grid, device_group(g),
+                                            plan->dtype, plan->d_partials, state->d, partial_out,
                                             static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm partial launch");
     plan->partial_pending = true;
     plan->norm_pending = false;
     plan->norm_state = state;
-    plan->norm_last = last;
-    plan->norm_w_last = wl;
-    plan->norm_last_is_first = last_is_first ? 1 : 0;
+    plan->norm_group = g;
     return ok();
 }
 
@@ -813,57 +913,11 @@ mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, fl
     return ok();
 }
 
-namespace {
-
-mp_status adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, mpk::Weight w_last,
-                     int32_t last_is_first, const mp_adamw_hparams* hp, const Fp8Out* fp8,
-                     mp_stream stream)
-{
-    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
-    mp_status st = check_hparams(hp);
-    if (st != MP_OK) return st;
-    st = check_last(plan, last, w_last, last_is_first);
-    if (st != MP_OK) return st;
-    if (!plan->norm_pending || plan->norm_state != state || plan->norm_last != last ||
-        (last != nullptr && (!same_weight(plan->norm_w_last, w_last) ||
-                             plan->norm_last_is_first != (last_is_first ? 1 : 0))))
-        return fail(MP_ERR_ORDER, "the AdamW step must follow mp_unscale_check_norm on the same "
-                                  "plan and state, with the same last micro-batch arguments");
-    st = check_devices(plan, state);
-    if (st != MP_OK) return st;
-    mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
-    hipError_t e = mpk::launch_adamw(view(plan), plan->grid, last ? last->d_ptrs : nullptr, w_last,
-                                     grad_mode(last, last_is_first), plan->dtype, a, fp8, state->d,
-                                     static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "adamw launch");
-    plan->norm_pending = false;
-    return ok();
-}
-
-mp_status update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, mpk::Weight w_last,
-                      int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
-                      mp_stream stream)
-{
-    // every structural check first, so that an error enqueues nothing
-    if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
-    mp_status st = check_hparams(hp);
-    if (st == MP_OK) st = check_last(plan, last, w_last, last_is_first);
-    if (st == MP_OK && (std::isnan(max_norm) || std::isinf(max_norm)))
-        st = fail(MP_ERR_INVALID, "max_norm must be finite");
-    if (st == MP_OK) st = check_devices(plan, state);
-    if (st != MP_OK) return st;
-    st = unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream);
-    if (st == MP_OK) st = adamw_step(plan, state, last, w_last, last_is_first, hp, nullptr, stream);
-    if (st == MP_OK) st = mp_scaler_update(state, stream);
-    return st;
-}
-
-}  // namespace
-
 mp_status mp_adamw_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
                         int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
 {
-    return adamw_step(plan, state, last, host_weight(w_last), last_is_first, hp, nullptr, stream);
+    return adamw_step(plan, state, single(last, host_weight(w_last), last_is_first), hp, nullptr,
+                      stream);
 }
 
 mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
@@ -872,15 +926,16 @@ mp_status mp_adamw_step_fp8(mp_plan* plan, mp_state* state, const mp_gradset* la
 {
     if (fp8 == nullptr) return fail(MP_ERR_INVALID, "fp8 set is NULL");
     if (fp8->plan != plan) return fail(MP_ERR_INVALID, "fp8 set belongs to another plan");
-    return adamw_step(plan, state, last, host_weight(w_last), last_is_first, hp, fp8->d_out,
-                      stream);
+    return adamw_step(plan, state, single(last, host_weight(w_last), last_is_first), hp,
+                      fp8->d_out, stream);
 }
 
 mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
                          int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
                          mp_stream stream)
 {
-    return update_step(plan, state, last, host_weight(w_last), last_is_first, max_norm, hp, stream);
+    return update_step(plan, state, single(last, host_weight(w_last), last_is_first), max_norm,
+                       hp, stream);
 }
 
 mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* last,
@@ -888,8 +943,19 @@ mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* la
                             const mp_adamw_hparams* hp, mp_stream stream)
 {
     if (last != nullptr && w_last == nullptr) return fail(MP_ERR_INVALID, "w_last is NULL");
-    return update_step(plan, state, last, device_weight(w_last), last_is_first, max_norm, hp,
-                       stream);
+    return update_step(plan, state, single(last, device_weight(w_last), last_is_first), max_norm,
+                       hp, stream);
+}
+
+mp_status mp_update_step_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,
+                               const float* weights, int32_t n, int32_t weights_on_device,
+                               int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
+                               mp_stream stream)
+{
+    Group g;
+    mp_status st = make_group(sets, weights, n, weights_on_device, last_is_first, &g);
+    if (st != MP_OK) return st;
+    return update_step(plan, state, g, max_norm, hp, stream);
 }
 
 mp_status mp_scaler_update(mp_state* state, mp_stream stream)

@@ -105,6 +105,20 @@ struct Weight {
     const float* ptr;
 };
 
+// The 16-bit gradients one pass folds in, in micro-batch order: up to
+// kMaxGroup gradsets (device tables uint16_t*[n_tensors]) with their weights,
+// after the accumulator when `acc` is set.  Every term is added with the
+// roundings of one mp_accumulate call, so a group gives the bits of the same
+// micro-batches accumulated one by one.
+constexpr int kMaxGroup = 4;
+
+struct Grads {
+    const uint16_t* const* set[kMaxGroup];
+    Weight w[kMaxGroup];
+    int32_t n;        // 0 .. kMaxGroup gradsets
+    int32_t acc;      // 1: the accumulator is the first term
+};
+
 // FP8 (E4M3) outputs of one tensor for the fused AdamW pass: numel codes and
 // numel/16 block scales, or both NULL (the tensor is not cast).
 struct Fp8Out {
@@ -112,21 +126,16 @@ struct Fp8Out {
     float* scales;
 };
 
-// How the gradient of one element is formed (see mp_unscale_check_norm).
-enum GradMode { kAccOnly = 0, kLastOnly = 1, kAccPlusLast = 2 };
-
-hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, Weight w,
-                             int first, int dtype, hipStream_t s);
-hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
-                       int mode, int dtype, double* partials, float max_norm, DevState* st,
-                       hipStream_t s);
-hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* const* last,
-                               Weight w_last, int mode, int dtype, double* partials,
-                               const DevState* st, double* out, hipStream_t s);
+// accumulate: acc = the group's terms (first: without the accumulator), n >= 1
+hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int first, int dtype,
+                             hipStream_t s);
+hipError_t launch_norm(const PlanView& p, int grid, const Grads& g, int dtype, double* partials,
+                       float max_norm, DevState* st, hipStream_t s);
+hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int dtype,
+                               double* partials, const DevState* st, double* out, hipStream_t s);
 hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s);
-hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
-                        int mode, int dtype, const AdamArgs& a, const Fp8Out* fp8, DevState* st,
-                        hipStream_t s);
+hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, const AdamArgs& a,
+                        const Fp8Out* fp8, DevState* st, hipStream_t s);
 hipError_t launch_scaler(DevState* st, hipStream_t s);
 hipError_t launch_token_weights(const int64_t* counts, int k, float* weights, hipStream_t s);
 hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s);

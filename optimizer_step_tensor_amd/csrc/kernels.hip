@@ -193,16 +193,40 @@ __device__ __forceinline__ float weight_of(const Weight& w)
 }
 
 // The fp32 gradient of one element ("Megatron Internals III", section 8;
-// "Mixed precision ...", section 2 "Gradient accumulation"): the accumulated
-// buffer, the last micro-batch alone, or the last micro-batch added to the
-// buffer with the same two roundings mp_accumulate uses.
-template <int DT, int MODE>
-__device__ __forceinline__ float grad_eff(float acc, uint32_t h, float w_last)
+// "Mixed precision ...", section 2 "Gradient accumulation"): the accumulator
+// (ACC) followed by NG micro-batches in order, each added with the two
+// roundings of one accumulation step, x = fl(x + fl(w_i * widen(g_i))).
+// Without the accumulator the first term is fl(w_1 * widen(g_1)) itself, as
+// in a first accumulation (so a -0 stays -0).
+template <int DT, bool ACC, int NG>
+__device__ __forceinline__ float grad_sum(float acc, const uint32_t (&h)[kMaxGroup],
+                                          const float (&w)[kMaxGroup])
 {
-    if (MODE == kAccOnly) return acc;
-    const float contribution = w_last * widen16<DT>(h);
-    if (MODE == kLastOnly) return contribution;
-    return acc + contribution;
+    static_assert(ACC || NG > 0, "a gradient needs at least one term");
+    float x = acc;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const float t = w[i] * widen16<DT>(h[i]);
+        x = (ACC || i > 0) ? x + t : t;
+    }
+    return x;
+}
+
+// The group's weights, each read once per block.
+template <int NG>
+__device__ __forceinline__ void group_weights(const Grads& g, float (&w)[kMaxGroup])
+{
+#pragma unroll
+    for (int i = 0; i < kMaxGroup; ++i) w[i] = i < NG ? weight_of(g.w[i]) : 0.0f;
+}
+
+// Element k of group j of every set, in micro-batch order.
+template <int NG>
+__device__ __forceinline__ void element_terms(const H4 (&h)[kMaxGroup][kGroupsPerLane], int j, int k,
+                                              uint32_t (&out)[kMaxGroup])
+{
+#pragma unroll
+    for (int i = 0; i < kMaxGroup; ++i) out[i] = i < NG ? h[i][j].v[k] : 0u;
 }
 
 // Deterministic block sum of one double per lane (result valid in lane 0).
@@ -225,27 +249,29 @@ __device__ __forceinline__ double block_sum(double x)
 // ---------------------------------------------------------------------------
 // Accumulation of one micro-batch.
 // ---------------------------------------------------------------------------
-template <int DT, bool FIRST>
-__global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
-                                                       const uint16_t* const* __restrict__ g16,
-                                                       Weight wt)
+template <int DT, bool FIRST, int NG>
+__global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p, Grads g)
 {
-    const float w = weight_of(wt);
+    float w[kMaxGroup];
+    group_weights<NG>(g, w);
     for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
          c += gridDim.x) {
         const Chunk ch = p.chunks[c];
         float* acc = p.tensors[ch.tensor].acc + ch.start;
-        const uint16_t* g = g16[ch.tensor] + ch.start;
+        const uint16_t* gp[kMaxGroup];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) gp[i] = g.set[i][ch.tensor] + ch.start;
         for_each_pass(ch.len, [&](auto full, int base) {
             constexpr bool F = decltype(full)::value;
             int e[kGroupsPerLane], nv[kGroupsPerLane];
-            H4 h[kGroupsPerLane];
+            H4 h[kMaxGroup][kGroupsPerLane];
             F4 a[kGroupsPerLane];
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
                 e[j] = base + lane_offset(j);
                 nv[j] = F ? kGroup : valid_count(ch.len, e[j]);
-                h[j] = load_h4<F>(g + e[j], nv[j]);
+#pragma unroll
+                for (int i = 0; i < NG; ++i) h[i][j] = load_h4<F>(gp[i] + e[j], nv[j]);
                 if (!FIRST) a[j] = load_f4<F>(acc + e[j], nv[j]);
             }
 #pragma unroll
@@ -253,8 +279,9 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
                 F4 out;
 #pragma unroll
                 for (int k = 0; k < kGroup; ++k) {
-                    const float contribution = w * widen16<DT>(h[j].v[k]);
-                    out.v[k] = FIRST ? contribution : a[j].v[k] + contribution;
+                    uint32_t hk[kMaxGroup];
+                    element_terms<NG>(h, j, k, hk);
+                    out.v[k] = grad_sum<DT, !FIRST, NG>(FIRST ? 0.0f : a[j].v[k], hk, w);
                 }
                 store_f4<F>(acc + e[j], out, nv[j]);
             }
@@ -268,40 +295,42 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p,
 // NaN; finite fp32 squares cannot overflow binary64 for any element count a
 // device can hold, so the overflow flag is exactly "the sum is not finite".
 // ---------------------------------------------------------------------------
-template <int DT, int MODE>
-__global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p,
-                                                         const uint16_t* const* __restrict__ last,
-                                                         Weight wl,
+template <int DT, bool ACC, int NG>
+__global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p, Grads g,
                                                          const DevState* __restrict__ st,
                                                          double* __restrict__ partials)
 {
-    const float w_last = weight_of(wl);
+    float w[kMaxGroup];
+    group_weights<NG>(g, w);
     const float inv = st->inv_scale;
     double s = 0.0;
     for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
          c += gridDim.x) {
         const Chunk ch = p.chunks[c];
-        const float* acc = MODE == kLastOnly ? nullptr : p.tensors[ch.tensor].acc + ch.start;
-        const uint16_t* g = MODE == kAccOnly ? nullptr : last[ch.tensor] + ch.start;
+        const float* acc = ACC ? p.tensors[ch.tensor].acc + ch.start : nullptr;
+        const uint16_t* gp[kMaxGroup];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) gp[i] = g.set[i][ch.tensor] + ch.start;
         for_each_pass(ch.len, [&](auto full, int base) {
             constexpr bool F = decltype(full)::value;
             int nv[kGroupsPerLane];
             F4 a[kGroupsPerLane];
-            H4 h[kGroupsPerLane];
+            H4 h[kMaxGroup][kGroupsPerLane];
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
                 const int e = base + lane_offset(j);
                 nv[j] = F ? kGroup : valid_count(ch.len, e);
-                if (MODE != kLastOnly) a[j] = load_f4<F>(acc + e, nv[j]);
-                if (MODE != kAccOnly) h[j] = load_h4<F>(g + e, nv[j]);
+                if (ACC) a[j] = load_f4<F>(acc + e, nv[j]);
+#pragma unroll
+                for (int i = 0; i < NG; ++i) h[i][j] = load_h4<F>(gp[i] + e, nv[j]);
             }
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
 #pragma unroll
                 for (int k = 0; k < kGroup; ++k) {
-                    const float gv = grad_eff<DT, MODE>(MODE == kLastOnly ? 0.0f : a[j].v[k],
-                                                        MODE == kAccOnly ? 0u : h[j].v[k],
-                                                        w_last) * inv;
+                    uint32_t hk[kMaxGroup];
+                    element_terms<NG>(h, j, k, hk);
+                    const float gv = grad_sum<DT, ACC, NG>(ACC ? a[j].v[k] : 0.0f, hk, w) * inv;
                     const double d = static_cast<double>(gv);
                     // the square of an fp32 value is exact in binary64, so this
                     // fma is the same as a rounded add of the exact square; the
@@ -455,15 +484,14 @@ __device__ __forceinline__ void store_scale(float* p, float scale)
 // the new weights of every tensor that has FP8 outputs are also cast in blocks
 // of 16 exactly as k_fp8_blocks16 casts them, in the same pass.
 // ---------------------------------------------------------------------------
-template <int DT, int MODE, bool FP8>
-__global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
-                                                  const uint16_t* const* __restrict__ last,
-                                                  Weight wl, AdamArgs a,
+template <int DT, bool ACC, int NG, bool FP8>
+__global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs a,
                                                   const Fp8Out* __restrict__ fp8,
                                                   const DevState* __restrict__ st)
 {
     if (st->s.found_inf) return;                  // skipped step: write nothing
-    const float w_last = weight_of(wl);
+    float gw[kMaxGroup];
+    group_weights<NG>(g, gw);
     const float scale = st->update_scale;
     const float bc1 = static_cast<float>(1.0 - st->s.beta1_pow * static_cast<double>(a.beta1));
     const float bc2 = static_cast<float>(1.0 - st->s.beta2_pow * static_cast<double>(a.beta2));
@@ -475,8 +503,10 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
         const Chunk ch = p.chunks[c];
         const TensorDesc td = p.tensors[ch.tensor];
         const float lam = a.weight_decay * td.wd_mult;
-        const float* acc = MODE == kLastOnly ? nullptr : td.acc + ch.start;
-        const uint16_t* g = MODE == kAccOnly ? nullptr : last[ch.tensor] + ch.start;
+        const float* acc = ACC ? td.acc + ch.start : nullptr;
+        const uint16_t* gp[kMaxGroup];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) gp[i] = g.set[i][ch.tensor] + ch.start;
         float* mw = td.master + ch.start;
         float* mm = td.m + ch.start;
         float* mv = td.v + ch.start;
@@ -496,13 +526,14 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
             constexpr bool F = decltype(full)::value;
             int e[kGroupsPerLane], nv[kGroupsPerLane];
             F4 ga[kGroupsPerLane], wv[kGroupsPerLane], m[kGroupsPerLane], v[kGroupsPerLane];
-            H4 h[kGroupsPerLane];
+            H4 h[kMaxGroup][kGroupsPerLane];
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
                 e[j] = base + lane_offset(j);
                 nv[j] = F ? kGroup : valid_count(ch.len, e[j]);
-                if (MODE != kLastOnly) ga[j] = load_f4<F>(acc + e[j], nv[j]);
-                if (MODE != kAccOnly) h[j] = load_h4<F>(g + e[j], nv[j]);
+                if (ACC) ga[j] = load_f4<F>(acc + e[j], nv[j]);
+#pragma unroll
+                for (int i = 0; i < NG; ++i) h[i][j] = load_h4<F>(gp[i] + e[j], nv[j]);
                 wv[j] = load_f4<F>(mw + e[j], nv[j]);
                 m[j] = load_f4<F>(mm + e[j], nv[j]);
                 v[j] = load_f4<F>(mv + e[j], nv[j]);
@@ -512,8 +543,9 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p,
                 H4 out16;
 #pragma unroll
                 for (int k = 0; k < kGroup; ++k) {
-                    const float gr = grad_eff<DT, MODE>(MODE == kLastOnly ? 0.0f : ga[j].v[k],
-                                                        MODE == kAccOnly ? 0u : h[j].v[k], w_last);
+                    uint32_t hk[kMaxGroup];
+                    element_terms<NG>(h, j, k, hk);
+                    const float gr = grad_sum<DT, ACC, NG>(ACC ? ga[j].v[k] : 0.0f, hk, gw);
                     const float gs = gr * scale;
                     const float mj = b1 * m[j].v[k] + ob1 * gs;
                     const float vj = b2 * v[j].v[k] + ob2 * (gs * gs);
@@ -710,50 +742,65 @@ unsigned elementwise_grid(int64_t n)
     return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
 }
 
-template <int DT, int MODE>
-void launch_norm_t(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
-                   double* partials, DevState* st, hipStream_t s)
+// Calls fn(dt, acc, ng) with the three as compile-time constants, for the
+// plan's 16-bit format, whether the accumulator is a term, and the group size.
+template <int DT, bool ACC, class Fn>
+bool with_count(int n, Fn&& fn)
 {
-    k_norm_partial<DT, MODE><<<grid, kBlock, 0, s>>>(p, last, w_last, st, partials);
+    using std::integral_constant;
+    switch (n) {
+    case 0:
+        if constexpr (ACC) {
+            fn(integral_constant<int, DT>{}, std::bool_constant<ACC>{}, integral_constant<int, 0>{});
+            return true;
+        }
+        return false;
+    case 1: fn(integral_constant<int, DT>{}, std::bool_constant<ACC>{}, integral_constant<int, 1>{}); return true;
+    case 2: fn(integral_constant<int, DT>{}, std::bool_constant<ACC>{}, integral_constant<int, 2>{}); return true;
+    case 3: fn(integral_constant<int, DT>{}, std::bool_constant<ACC>{}, integral_constant<int, 3>{}); return true;
+    case 4: fn(integral_constant<int, DT>{}, std::bool_constant<ACC>{}, integral_constant<int, 4>{}); return true;
+    default: return false;
+    }
 }
 
-template <int DT, int MODE>
-void launch_adamw_t(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
-                    const AdamArgs& a, const Fp8Out* fp8, DevState* st, hipStream_t s)
+template <class Fn>
+hipError_t with_group(int dtype, const Grads& g, Fn&& fn)
 {
-    if (fp8 != nullptr) k_adamw<DT, MODE, true><<<grid, kBlock, 0, s>>>(p, last, w_last, a, fp8, st);
-    else                k_adamw<DT, MODE, false><<<grid, kBlock, 0, s>>>(p, last, w_last, a, fp8, st);
+    bool ok;
+    if (dtype == MP_BF16) ok = g.acc ? with_count<MP_BF16, true>(g.n, fn) : with_count<MP_BF16, false>(g.n, fn);
+    else                  ok = g.acc ? with_count<MP_FP16, true>(g.n, fn) : with_count<MP_FP16, false>(g.n, fn);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_blocks(const PlanView& p, int grid, const Grads& g, int dtype,
+                              double* partials, const DevState* st, hipStream_t s)
+{
+    return with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
+        k_norm_partial<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value>
+            <<<grid, kBlock, 0, s>>>(p, g, st, partials);
+    });
 }
 
 }  // namespace
 
-hipError_t launch_accumulate(const PlanView& p, int grid, const uint16_t* const* g16, Weight w,
-                             int first, int dtype, hipStream_t s)
+hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int first, int dtype,
+                             hipStream_t s)
 {
-    if (dtype == MP_BF16) {
-        if (first) k_accumulate<MP_BF16, true><<<grid, kBlock, 0, s>>>(p, g16, w);
-        else       k_accumulate<MP_BF16, false><<<grid, kBlock, 0, s>>>(p, g16, w);
-    } else {
-        if (first) k_accumulate<MP_FP16, true><<<grid, kBlock, 0, s>>>(p, g16, w);
-        else       k_accumulate<MP_FP16, false><<<grid, kBlock, 0, s>>>(p, g16, w);
-    }
-    return hipGetLastError();
+    if (g.n < 1 || g.acc) return hipErrorInvalidValue;
+    // the accumulator is read unless this is the first accumulation
+    Grads gg = g;
+    gg.acc = first ? 0 : 1;
+    return with_group(dtype, gg, [&](auto dt, auto acc, auto ng) {
+        if constexpr (decltype(ng)::value > 0)
+            k_accumulate<decltype(dt)::value, !decltype(acc)::value, decltype(ng)::value>
+                <<<grid, kBlock, 0, s>>>(p, gg);
+    });
 }
 
-hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
-                       int mode, int dtype, double* partials, float max_norm, DevState* st,
-                       hipStream_t s)
+hipError_t launch_norm(const PlanView& p, int grid, const Grads& g, int dtype, double* partials,
+                       float max_norm, DevState* st, hipStream_t s)
 {
-    if (dtype == MP_BF16) {
-        if (mode == kAccOnly)       launch_norm_t<MP_BF16, kAccOnly>(p, grid, last, w_last, partials, st, s);
-        else if (mode == kLastOnly) launch_norm_t<MP_BF16, kLastOnly>(p, grid, last, w_last, partials, st, s);
-        else                        launch_norm_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, partials, st, s);
-    } else {
-        if (mode == kAccOnly)       launch_norm_t<MP_FP16, kAccOnly>(p, grid, last, w_last, partials, st, s);
-        else if (mode == kLastOnly) launch_norm_t<MP_FP16, kLastOnly>(p, grid, last, w_last, partials, st, s);
-        else                        launch_norm_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, partials, st, s);
-    }
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_norm_blocks(p, grid, g, dtype, partials, st, s);
     if (err != hipSuccess) return err;
     const int n2 = grid < kNormStage2 ? grid : kNormStage2;
     k_norm_stage2<<<n2, kBlock, 0, s>>>(partials, grid, partials + grid);
@@ -761,21 +808,10 @@ hipError_t launch_norm(const PlanView& p, int grid, const uint16_t* const* last,
     return hipGetLastError();
 }
 
-hipError_t launch_norm_partial(const PlanView& p, int grid, const uint16_t* const* last,
-                               Weight w_last, int mode, int dtype, double* partials,
-                               const DevState* st, double* out, hipStream_t s)
+hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int dtype,
+                               double* partials, const DevState* st, double* out, hipStream_t s)
 {
-    DevState* stm = const_cast<DevState*>(st);
-    if (dtype == MP_BF16) {
-        if (mode == kAccOnly)       launch_norm_t<MP_BF16, kAccOnly>(p, grid, last, w_last, partials, stm, s);
-        else if (mode == kLastOnly) launch_norm_t<MP_BF16, kLastOnly>(p, grid, last, w_last, partials, stm, s);
-        else                        launch_norm_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, partials, stm, s);
-    } else {
-        if (mode == kAccOnly)       launch_norm_t<MP_FP16, kAccOnly>(p, grid, last, w_last, partials, stm, s);
-        else if (mode == kLastOnly) launch_norm_t<MP_FP16, kLastOnly>(p, grid, last, w_last, partials, stm, s);
-        else                        launch_norm_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, partials, stm, s);
-    }
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_norm_blocks(p, grid, g, dtype, partials, st, s);
     if (err != hipSuccess) return err;
     const int n2 = grid < kNormStage2 ? grid : kNormStage2;
     k_norm_stage2<<<n2, kBlock, 0, s>>>(partials, grid, partials + grid);
@@ -789,20 +825,24 @@ hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, 
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(const PlanView& p, int grid, const uint16_t* const* last, Weight w_last,
-                        int mode, int dtype, const AdamArgs& a, const Fp8Out* fp8, DevState* st,
-                        hipStream_t s)
+hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, const AdamArgs& a,
+                        const Fp8Out* fp8, DevState* st, hipStream_t s)
 {
-    if (dtype == MP_BF16) {
-        if (mode == kAccOnly)       launch_adamw_t<MP_BF16, kAccOnly>(p, grid, last, w_last, a, fp8, st, s);
-        else if (mode == kLastOnly) launch_adamw_t<MP_BF16, kLastOnly>(p, grid, last, w_last, a, fp8, st, s);
-        else                        launch_adamw_t<MP_BF16, kAccPlusLast>(p, grid, last, w_last, a, fp8, st, s);
+    hipError_t err;
+    if (fp8 != nullptr) {
+        // the fused FP8 cast is built for a single last micro-batch
+        if (g.n > 1) return hipErrorInvalidValue;
+        err = with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
+            if constexpr (decltype(ng)::value <= 1)
+                k_adamw<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value, true>
+                    <<<grid, kBlock, 0, s>>>(p, g, a, fp8, st);
+        });
     } else {
-        if (mode == kAccOnly)       launch_adamw_t<MP_FP16, kAccOnly>(p, grid, last, w_last, a, fp8, st, s);
-        else if (mode == kLastOnly) launch_adamw_t<MP_FP16, kLastOnly>(p, grid, last, w_last, a, fp8, st, s);
-        else                        launch_adamw_t<MP_FP16, kAccPlusLast>(p, grid, last, w_last, a, fp8, st, s);
+        err = with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
+            k_adamw<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value, false>
+                <<<grid, kBlock, 0, s>>>(p, g, a, fp8, st);
+        });
     }
-    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     k_adam_clock<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
     return hipGetLastError();

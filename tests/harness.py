@@ -99,6 +99,9 @@ class DeviceRun:
         self.device_weights = False        # True: weights from device counts, steps use the
         self.dev_counts = None             # *_dw entry points (kept alive until the next step)
         self.dev_weights = None
+        # (accumulate groups, folded group) of micro-batch indices: steps use
+        # mp_accumulate_group per group, then mp_update_step_group on the folded one
+        self.schedule = None
 
     def stats(self):
         return self.mp.read_stats(self.state)
@@ -121,6 +124,8 @@ class DeviceRun:
         mp, w, s = self.mp, self.w, self.step_no
         assert len(self.g16) == w.k, "per-micro-batch buffers needed to run a step"
         self.fill_grads(s, scale)
+        if self.schedule is not None:
+            return self._step_groups(s)
         if self.device_weights:
             return self._step_device_weights(s, snapshot)
         weights = mp.mp_token_weights(w.token_counts(s))
@@ -149,6 +154,32 @@ class DeviceRun:
                                  self.fp8set)
         mp.mp_scaler_update(self.state)
         return acc_snapshot
+
+    def _step_groups(self, s):
+        """The step with resident micro-batches folded in groups; with device_weights the
+        group calls read the weights from mp_token_weights_dev's output."""
+        torch, mp, w = self.torch, self.mp, self.w
+        acc_groups, fold = self.schedule
+        order = [i for g in acc_groups for i in g] + list(fold)
+        assert order == list(range(w.k)), self.schedule
+        counts = w.token_counts(s)
+        if self.device_weights:
+            self.dev_counts = torch.tensor(counts, dtype=torch.int64, device="cuda")
+            self.dev_weights = torch.empty(w.k, dtype=torch.float32, device="cuda")
+            mp.mp_token_weights_dev(w.k, self.dev_counts, self.dev_weights)
+
+            def wts(grp):
+                return self.dev_weights.data_ptr() + 4 * grp[0]
+        else:
+            host = mp.mp_token_weights(counts)
+
+            def wts(grp):
+                return [host[i] for i in grp]
+        for n, grp in enumerate(acc_groups):
+            mp.mp_accumulate_group(self.model.plan, [self.gsets[i] for i in grp], wts(grp), n == 0)
+        mp.mp_update_step_group(self.model.plan, self.state, [self.gsets[i] for i in fold],
+                                wts(fold), not acc_groups, w.max_norm, self.hp)
+        return None
 
     def _step_device_weights(self, s, snapshot):
         """The step with n_i in device memory: mp_token_weights_dev, mp_accumulate_dw and

@@ -28,6 +28,19 @@ def test_step_bytes_follow_the_schedule():
     assert b1["step"] == 30 and b1["norm"] + b1["adamw"] == 30 and b1["adamw"] == 28
 
 
+def test_group_bytes_reduce_to_the_one_at_a_time_schedule():
+    """Groups of one micro-batch give the one-at-a-time step's 10k + 24 bytes, and k = 1 its 30;
+    folding resident micro-batches saves the accumulator's round trips: for k = 4, 50 bytes with
+    two accumulated in one pass, and 42 with all four folded into the norm and AdamW."""
+    for k in (2, 3, 4, 8):
+        ones = [[i] for i in range(k - 1)]
+        assert bench.group_bytes_per_param(ones, [k - 1]) == bench.bytes_per_param(k)["step"]
+    assert bench.group_bytes_per_param([], [0]) == bench.bytes_per_param(1)["step"] == 30
+    assert bench.group_bytes_per_param([[0, 1]], [2, 3]) == 8 + 8 + 34 == 50
+    assert bench.group_bytes_per_param([], [0, 1, 2, 3]) == 8 + 34 == 42
+    assert bench.group_bytes_per_param([[0, 1, 2, 3]], [4, 5, 6, 7]) == 12 + 12 + 38 == 62
+
+
 def test_adamw_bytes_are_the_state_it_touches():
     """AdamW reads acc (4), the last 16-bit gradient (2), master, m, v (12) and writes master, m,
     v (12) and the 16-bit weight (2): every byte of the 20-byte state except the gradient buffers

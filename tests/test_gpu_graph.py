@@ -54,3 +54,48 @@ def test_graph_replays_equal_eager_steps(form):
         del g
         eager.close()
         graphed.close()
+
+
+def test_graph_replays_follow_the_scaler():
+    """One captured step on the fp16 edge list (dynamic S, growth every 2 clean steps, an inf at
+    step 2), replayed for every step with new gradients and new device token counts written
+    between replays: each replay equals the oracle's step, through the skip, the backoff and
+    the growth, so the scaler's decisions live on the device and nothing captured goes stale."""
+    import torch
+    import optimizer_step_tensor_amd as mp
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make("edges-fp16")
+    orc, dev = OracleRun(w), DeviceRun(w)
+    k = w.k
+    cnt = torch.ones(k, dtype=torch.int64, device="cuda")
+    wts = torch.empty(k, dtype=torch.float32, device="cuda")
+    wp = [wts.data_ptr() + 4 * i for i in range(k)]
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        st = torch.cuda.current_stream()
+        plan = dev.model.plan
+        mp.mp_token_weights_dev(k, cnt, wts, st)
+        for i in range(k - 1):
+            mp.mp_accumulate_dw(plan, dev.gsets[i], wp[i], i == 0, st)
+        mp.mp_update_step_dw(plan, dev.state, dev.gsets[-1], wp[-1], 0, w.max_norm, dev.hp, st)
+    try:
+        seen = set()
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            assert dev.stats()["scale"] == scale
+            orc.step()
+            dev.fill_grads(s, scale)
+            cnt.copy_(torch.tensor(w.token_counts(s), dtype=torch.int64))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            rep = compare_step(dev, orc, w, s)
+            seen.add("skip" if rep["found_inf"] else "clean")
+            print("  replay", s, rep, flush=True)
+        assert seen == {"skip", "clean"}
+        assert dev.stats()["scale"] != w.scaler["init_scale"]
+    finally:
+        del g
+        dev.close()

@@ -170,6 +170,19 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_update_step_dw(None, None, None, dev, 0, 1.0, None, None) == mp.MP_ERR_INVALID
     assert (L.mp_update_step_dw(fake_state, fake_state, fake_state, None, 0, 1.0, None, None)
             == mp.MP_ERR_INVALID)
+    # group entry points: the group's size, NULL arrays and NULL members are refused first
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    two = ctypes.cast((ctypes.c_void_p * 2)(0x10000, None), PP)
+    wts = (ctypes.c_float * 2)(0.5, 0.5)
+    for n in (0, 5, -1):
+        assert L.mp_accumulate_group(fake_state, two, wts, n, 0, 1, None) == mp.MP_ERR_INVALID
+        assert (L.mp_update_step_group(fake_state, fake_state, two, wts, n, 0, 1, 1.0, None, None)
+                == mp.MP_ERR_INVALID)
+    assert L.mp_accumulate_group(fake_state, None, wts, 2, 0, 1, None) == mp.MP_ERR_INVALID
+    assert L.mp_accumulate_group(fake_state, two, None, 2, 0, 1, None) == mp.MP_ERR_INVALID
+    assert L.mp_accumulate_group(None, two, wts, 2, 0, 1, None) == mp.MP_ERR_INVALID
+    assert (L.mp_update_step_group(None, None, two, wts, 2, 0, 1, 1.0, None, None)
+            == mp.MP_ERR_INVALID)
 
 
 def test_bench_refuses_more_than_one_gpu():
