@@ -204,8 +204,13 @@ def time_save_restore(mp, torch, state, stream, reps=20):
             "import_us": (t2 - t1) / reps * 1e6}
 
 
-def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
-    """The rows after the hot path, on the same resident buffers:
+EXTRAS = ("device_copy", "fp8_block_cast", "adamw_fp8_fused", "state_save_restore",
+          "zero8_rank_share", "resident_groups")
+
+
+def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=None):
+    """The rows after the hot path, on the same resident buffers (`only`: a subset of EXTRAS):
+    - the runtime's own device-to-device copy of 4 GiB, context for the roofline;
     - the fine-grained FP8 cast (block 16) of every fp32 master;
     - the same cast fused into the AdamW pass (mp_adamw_step_fp8), against the plain AdamW pass
       timed the same way in alternation;
@@ -215,17 +220,34 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
     - the step with k <= 4 micro-batch gradients resident, folded in groups: two accumulated in
       one pass and two folded into the norm and AdamW passes, or all k folded there (no
       accumulator pass at all).  Same results, bit for bit, as the timed step."""
-    sets_main = sets
+    def want(name):
+        return only is None or name in only
+
     out = {}
-    P, k = w.total, w.k
-    # context for the roofline: the runtime's own device-to-device copy of 4 GiB
-    a = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    ms = time_launches(torch, stream, lambda: b.copy_(a), 5)
-    out["device_copy"] = {"bytes_read": 4 << 30, "bytes_written": 4 << 30, "ms": ms,
-                          "GBps": 2 * (4 << 30) / ms / 1e6,
-                          "frac": 2 * (4 << 30) / ms / 1e6 / HBM_PEAK_GBPS}
-    del a, b
+    if want("device_copy"):
+        a = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        ms = time_launches(torch, stream, lambda: b.copy_(a), 5)
+        out["device_copy"] = {"bytes_read": 4 << 30, "bytes_written": 4 << 30, "ms": ms,
+                              "GBps": 2 * (4 << 30) / ms / 1e6,
+                              "frac": 2 * (4 << 30) / ms / 1e6 / HBM_PEAK_GBPS}
+        del a, b
+    if want("fp8_block_cast"):
+        out["fp8_block_cast"] = time_fp8_cast(mp, torch, w, model, stream)
+    if want("adamw_fp8_fused"):
+        out["adamw_fp8_fused"] = time_fused_fp8(mp, torch, w, model, sets, state, hp, weights,
+                                                stream)
+    if want("state_save_restore"):
+        out["state_save_restore"] = time_save_restore(mp, torch, state, stream)
+    if want("zero8_rank_share"):
+        out["zero8_rank_share"] = time_rank_share(mp, torch, w, model, g16, hp, weights, stream)
+    if want("resident_groups") and 2 <= w.k <= 4:
+        out["resident_groups"] = time_groups(mp, torch, w, model, sets, state, hp, weights,
+                                             stream)
+    return out
+
+
+def time_fp8_cast(mp, torch, w, model, stream):
     big = max(w.numels)
     codes = torch.empty(big, dtype=torch.uint8, device="cuda")
     scales = torch.empty(big // 16 + 1, dtype=torch.float32, device="cuda")
@@ -238,11 +260,12 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
     ms = time_launches(torch, stream, fp8_all, 3)
     n_cast = sum(n for _, n in cast)
     gbps = n_cast * (4 + 1 + 4 / 16) / ms / 1e6
-    out["fp8_block_cast"] = {"block": 16, "elements": n_cast, "ms": ms,
-                             "bytes_per_element": 5.25, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
-    del codes, scales
-    out["adamw_fp8_fused"] = time_fused_fp8(mp, torch, w, model, sets, state, hp, weights, stream)
-    out["state_save_restore"] = time_save_restore(mp, torch, state, stream)
+    return {"block": 16, "elements": n_cast, "ms": ms, "bytes_per_element": 5.25, "GBps": gbps,
+            "frac": gbps / HBM_PEAK_GBPS}
+
+
+def time_rank_share(mp, torch, w, model, g16, hp, weights, stream):
+    k = w.k
     ranks, r = 8, 0
     numel, ptrs = [], {"acc": [], "master": [], "m": [], "v": [], "w16": []}
     gp = [[] for _ in range(k)]
@@ -273,17 +296,12 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream):
 
     ms = time_launches(torch, stream, shard_step, 3)
     p_share = sum(numel)
-    out["zero8_rank_share"] = {"params": p_share, "ms_per_step": ms,
-                               "params_per_s": p_share / (ms * 1e-3),
-                               "GBps": bytes_per_param(k)["step"] * p_share / ms / 1e6}
     for g in sets:
         mp.mp_gradset_destroy(g)
     mp.mp_state_destroy(st)
     mp.mp_plan_destroy(plan)
-    if 2 <= k <= 4:
-        out["resident_groups"] = time_groups(mp, torch, w, model, sets_main, state, hp, weights,
-                                             stream)
-    return out
+    return {"params": p_share, "ms_per_step": ms, "params_per_s": p_share / (ms * 1e-3),
+            "GBps": bytes_per_param(k)["step"] * p_share / ms / 1e6}
 
 
 def group_bytes_per_param(acc_groups, fold):
@@ -334,7 +352,9 @@ def main():
     ap.add_argument("--trace-steps", type=int, default=0,
                     help="time this many single steps after warm-up and print each")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the FP8 block cast and one ZeRO-8 rank's slice")
+                    help="skip the measurements after the hot path (extras)")
+    ap.add_argument("--extras", default=None,
+                    help="comma-separated subset of the extras to run: " + ", ".join(EXTRAS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (for counter calibration)")
     ap.add_argument("--cold", action="store_true",
@@ -346,6 +366,14 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    only = None
+    if args.extras:
+        only = set(args.extras.split(","))
+        unknown = only - set(EXTRAS)
+        if unknown:
+            print("unknown extras: %s (known: %s)" % (", ".join(sorted(unknown)), ", ".join(EXTRAS)),
+                  file=sys.stderr)
+            sys.exit(2)
 
     import torch
     import inputs
@@ -514,7 +542,7 @@ def main():
            HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
 
     extras = None if args.no_extras else run_extras(mp, torch, w, model, g16, sets, state, hp,
-                                                    weights, stream)
+                                                    weights, stream, only)
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,

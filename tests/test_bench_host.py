@@ -56,3 +56,10 @@ def test_more_than_one_gpu_is_refused_without_touching_a_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "4"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and r.stdout == ""
+
+
+def test_unknown_extras_are_refused_before_any_work():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extras",
+                        "resident_groups,nonsense"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and r.stdout == "" and "nonsense" in r.stderr
