@@ -1,9 +1,10 @@
 """Throughput of the fused mixed-precision update step on one MI355X.
 
 One step = one logical update of the whole hot path over one batch of synthetic
-input: token weights, micro-batches 1..k-1 accumulated into the fp32 buffers,
-the last micro-batch folded into the unscale/overflow/norm pass and into the
-AdamW + RNE-cast pass, then the loss-scaler decision.  Inputs (fp32 masters,
+input: token weights (on the device, from device-resident target counts),
+micro-batches 1..k-1 accumulated into the fp32 buffers, the last micro-batch
+folded into the unscale/overflow/norm pass and into the AdamW + RNE-cast pass,
+then the loss-scaler decision.  Inputs (fp32 masters,
 per-micro-batch bf16 gradients) are generated on the device before the timed
 region and stay resident in HBM.
 
@@ -16,6 +17,7 @@ sample.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--graph] [--gpus 1]
 """
 import argparse
+import ctypes
 import gc
 import hashlib
 import json
@@ -341,8 +343,8 @@ def time_groups(mp, torch, w, model, sets, state, hp, weights, stream, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3-8B")
     ap.add_argument("--layout", default="flat", choices=("tensor", "flat"),
                     help="one allocation per tensor, or one flat buffer per kind of array")
@@ -402,9 +404,18 @@ def main():
             inputs.fill_dev_u16(x, w.grad_recipe(1, i, t, S0), w.dtype)
     sets = [model.gradset(g) for g in g16]
     hp = mp.adamw_hparams(**w.hp)
-    weights = mp.mp_token_weights(w.token_counts(1))
+    counts = w.token_counts(1)
+    weights = mp.mp_token_weights(counts)        # host weights, for the extras
     plan = model.plan
     stream = torch.cuda.current_stream()
+    # the step's token weights are computed on the device from device-resident counts, and
+    # every pass reads its weight there: the whole step is stream-ordered device work
+    counts_dev = torch.tensor(counts, dtype=torch.int64, device="cuda")
+    weights_dev = torch.empty(k, dtype=torch.float32, device="cuda")
+    L = mp.lib()
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    one = [ctypes.cast((ctypes.c_void_p * 1)(x.value), PP) for x in sets]   # groups of one
+    wptr = [ctypes.c_void_p(weights_dev.data_ptr() + 4 * i) for i in range(k)]
     info = mp.mp_plan_info(plan)
     log("plan:", info, "| resident %.1f GB" % (torch.cuda.memory_allocated() / 1e9))
 
@@ -441,18 +452,21 @@ def main():
                 ev[name].append((e0, e1))
             else:
                 fn()
-        lif = k == 1
+        lif = int(k == 1)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        chk = mp._check
+        chk(L.mp_token_weights_dev(k, counts_dev.data_ptr(), weights_dev.data_ptr(), sp))
         for i in range(k - 1):
-            timed("accumulate", lambda i=i: mp.mp_accumulate(plan, sets[i], weights[i], i == 0,
-                                                             stream))
+            timed("accumulate", lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1, 1,
+                                                                      int(i == 0), sp)))
         if record:                            # the fused step: norm + AdamW + scaler
             f0 = take()
             f0.record(stream)
-        timed("norm", lambda: mp.mp_unscale_check_norm(plan, state, sets[-1], weights[-1], lif,
-                                                       w.max_norm, stream))
-        timed("adamw", lambda: mp.mp_adamw_step(plan, state, sets[-1], weights[-1], lif, hp,
-                                                stream))
-        mp.mp_scaler_update(state, stream)
+        timed("norm", lambda: chk(L.mp_unscale_check_norm_group(plan, state, one[-1], wptr[-1], 1,
+                                                                 1, lif, w.max_norm, sp)))
+        timed("adamw", lambda: chk(L.mp_adamw_step_group(plan, state, one[-1], wptr[-1], 1, 1,
+                                                         lif, ctypes.byref(hp), sp)))
+        chk(L.mp_scaler_update(state, sp))
         if record:
             f1 = take()
             f1.record(stream)
@@ -563,8 +577,8 @@ def main():
                    "kernel_events": "inside the timed region" if record else
                                     "eager steps after the timed graph replays",
                    "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
-                   "schedule": "k-1 accumulate passes, last micro-batch folded into norm and "
-                               "AdamW passes",
+                   "schedule": "token weights from device counts; k-1 accumulate passes; the "
+                               "last micro-batch folded into the norm and AdamW passes",
                    "step_bytes_per_param": bpp["step"],
                    "step_GBps": step_bytes / ms_per_step / 1e6,
                    "step_hbm_frac": step_bytes / ms_per_step / 1e6 / HBM_PEAK_GBPS,

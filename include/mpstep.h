@@ -245,13 +245,6 @@ mp_status mp_state_scale_ptr(const mp_state* state, const float** dev_scale);
 mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int32_t first,
                         mp_stream stream);
 
-/* mp_accumulate with the weight read on the device from *weight (fp32, 4-byte
- * aligned device memory, e.g. an element of mp_token_weights_dev's output),
- * when the kernel runs.  The value is not checked on the host: a non-finite
- * weight makes the step overflow and be skipped. */
-mp_status mp_accumulate_dw(mp_plan* plan, const mp_gradset* g16, const float* weight,
-                           int32_t first, mp_stream stream);
-
 /* Accumulate n resident micro-batches (1 <= n <= 4) in one pass, for a caller
  * that keeps several micro-batch gradients in device memory at once.  The
  * result is bit for bit that of n mp_accumulate calls in array order (the
@@ -342,14 +335,6 @@ mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last,
                          int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
                          mp_stream stream);
 
-/* mp_update_step with w_last read on the device from *w_last (fp32, 4-byte
- * aligned device memory), as in mp_accumulate_dw; the norm and the AdamW pass
- * read the same address, so they see the same value.  w_last may be NULL only
- * when last is NULL. */
-mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* last,
-                            const float* w_last, int32_t last_is_first, float max_norm,
-                            const mp_adamw_hparams* hp, mp_stream stream);
-
 /* mp_update_step with the last n micro-batches (1 <= n <= 4) resident and all
  * folded into the norm pass and the AdamW pass, as `last` is folded in for
  * n = 1.  The gradient of each element is the accumulator (skipped when
@@ -365,6 +350,19 @@ mp_status mp_update_step_group(mp_plan* plan, mp_state* state, const mp_gradset*
                                const float* weights, int32_t n, int32_t weights_on_device,
                                int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
                                mp_stream stream);
+
+/* The two halves of mp_update_step_group before the scaler, for callers that
+ * time or interleave them: mp_unscale_check_norm and mp_adamw_step over the
+ * same group (same sets, weights and last_is_first, else MP_ERR_ORDER, as for
+ * the single-`last` forms).  With n = 1 and weights_on_device these are the
+ * single-`last` calls with the weight read on the device. */
+mp_status mp_unscale_check_norm_group(mp_plan* plan, mp_state* state,
+                                      const mp_gradset* const* sets, const float* weights,
+                                      int32_t n, int32_t weights_on_device, int32_t last_is_first,
+                                      float max_norm, mp_stream stream);
+mp_status mp_adamw_step_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,
+                              const float* weights, int32_t n, int32_t weights_on_device,
+                              int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream);
 
 /* Elementwise casts with the step's conversions: dst = round-to-nearest-even
  * of src into the 16-bit format (as in mp_adamw_step), and dst = exact fp32

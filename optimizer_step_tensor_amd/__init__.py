@@ -31,8 +31,8 @@ ENTRY_POINTS = [
     "mp_adamw_step", "mp_scaler_update", "mp_cast_to_16", "mp_widen_16",
     "mp_state_export", "mp_state_import", "mp_norm_partial", "mp_norm_finish",
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
-    "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_dw",
-    "mp_update_step_dw", "mp_accumulate_group", "mp_update_step_group",
+    "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_group",
+    "mp_update_step_group", "mp_unscale_check_norm_group", "mp_adamw_step_group",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -120,11 +120,12 @@ def _bind(L):
         "mp_gradset_update": ([P, PP, P], i32),
         "mp_update_step": ([P, P, P, f32, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
         "mp_token_weights_dev": ([i32, P, P, P], i32),
-        "mp_accumulate_dw": ([P, P, P, i32, P], i32),
-        "mp_update_step_dw": ([P, P, P, P, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
         "mp_accumulate_group": ([P, PP, P, i32, i32, i32, P], i32),
         "mp_update_step_group": ([P, P, PP, P, i32, i32, i32, f32, ctypes.POINTER(AdamWHparams),
                                   P], i32),
+        "mp_unscale_check_norm_group": ([P, P, PP, P, i32, i32, i32, f32, P], i32),
+        "mp_adamw_step_group": ([P, P, PP, P, i32, i32, i32, ctypes.POINTER(AdamWHparams), P],
+                                i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -275,18 +276,17 @@ def mp_accumulate(plan, gradset, weight, first, stream=None):
     _check(lib().mp_accumulate(plan, gradset, float(weight), int(bool(first)), _stream(stream)))
 
 
-def mp_accumulate_dw(plan, gradset, weight, first, stream=None):
-    """weight: the device address of one fp32 (a tensor element or an int)."""
-    _check(lib().mp_accumulate_dw(plan, gradset, _addr(weight), int(bool(first)),
-                                  _stream(stream)))
-
-
 def _group(sets, weights):
     """(gradset array, weight pointer, on_device) for the *_group entry points: weights is a
-    list of floats, or a device fp32 tensor (or a device address) holding len(sets) weights."""
+    list of floats (host), or a device fp32 tensor or an int device address where len(sets)
+    consecutive fp32 weights are read when the kernels run."""
     arr = (ctypes.c_void_p * len(sets))(*[s.value if isinstance(s, ctypes.c_void_p) else s
                                           for s in sets])
-    if isinstance(weights, (torch.Tensor, int)):
+    if isinstance(weights, torch.Tensor):
+        if not weights.is_cuda or weights.dtype != torch.float32:
+            raise TypeError("device weights must be a CUDA float32 tensor")
+        return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), _addr(weights), 1
+    if isinstance(weights, int):
         return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), _addr(weights), 1
     w = (ctypes.c_float * len(sets))(*[float(x) for x in weights])
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), ctypes.cast(w, ctypes.c_void_p), 0
@@ -314,10 +314,18 @@ def mp_update_step(plan, state, last, w_last, last_is_first, max_norm, hp, strea
                                 float(max_norm), ctypes.byref(hp), _stream(stream)))
 
 
-def mp_update_step_dw(plan, state, last, w_last, last_is_first, max_norm, hp, stream=None):
-    """w_last: the device address of one fp32 (a tensor element or an int)."""
-    _check(lib().mp_update_step_dw(plan, state, last, _addr(w_last), int(bool(last_is_first)),
-                                   float(max_norm), ctypes.byref(hp), _stream(stream)))
+def mp_unscale_check_norm_group(plan, state, sets, weights, last_is_first, max_norm,
+                                stream=None):
+    arr, w, dev = _group(sets, weights)
+    _check(lib().mp_unscale_check_norm_group(plan, state, arr, w, len(sets), dev,
+                                             int(bool(last_is_first)), float(max_norm),
+                                             _stream(stream)))
+
+
+def mp_adamw_step_group(plan, state, sets, weights, last_is_first, hp, stream=None):
+    arr, w, dev = _group(sets, weights)
+    _check(lib().mp_adamw_step_group(plan, state, arr, w, len(sets), dev,
+                                     int(bool(last_is_first)), ctypes.byref(hp), _stream(stream)))
 
 
 def mp_update_step_group(plan, state, sets, weights, last_is_first, max_norm, hp, stream=None):

@@ -832,14 +832,6 @@ mp_status mp_accumulate(mp_plan* plan, const mp_gradset* g16, float weight, int3
     return accumulate(plan, single(g16, host_weight(weight), 1), first, stream);
 }
 
-mp_status mp_accumulate_dw(mp_plan* plan, const mp_gradset* g16, const float* weight,
-                           int32_t first, mp_stream stream)
-{
-    if (weight == nullptr) return fail(MP_ERR_INVALID, "weight is NULL");
-    if (g16 == nullptr) return fail(MP_ERR_INVALID, "plan and gradset are required");
-    return accumulate(plan, single(g16, device_weight(weight), 1), first, stream);
-}
-
 mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, const float* weights,
                               int32_t n, int32_t weights_on_device, int32_t first,
                               mp_stream stream)
@@ -938,13 +930,25 @@ mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last,
                        hp, stream);
 }
 
-mp_status mp_update_step_dw(mp_plan* plan, mp_state* state, const mp_gradset* last,
-                            const float* w_last, int32_t last_is_first, float max_norm,
-                            const mp_adamw_hparams* hp, mp_stream stream)
+mp_status mp_unscale_check_norm_group(mp_plan* plan, mp_state* state,
+                                      const mp_gradset* const* sets, const float* weights,
+                                      int32_t n, int32_t weights_on_device, int32_t last_is_first,
+                                      float max_norm, mp_stream stream)
 {
-    if (last != nullptr && w_last == nullptr) return fail(MP_ERR_INVALID, "w_last is NULL");
-    return update_step(plan, state, single(last, device_weight(w_last), last_is_first), max_norm,
-                       hp, stream);
+    Group g;
+    mp_status st = make_group(sets, weights, n, weights_on_device, last_is_first, &g);
+    if (st != MP_OK) return st;
+    return unscale_check_norm(plan, state, g, max_norm, stream);
+}
+
+mp_status mp_adamw_step_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,
+                              const float* weights, int32_t n, int32_t weights_on_device,
+                              int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream)
+{
+    Group g;
+    mp_status st = make_group(sets, weights, n, weights_on_device, last_is_first, &g);
+    if (st != MP_OK) return st;
+    return adamw_step(plan, state, g, hp, nullptr, stream);
 }
 
 mp_status mp_update_step_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,

@@ -97,7 +97,7 @@ class DeviceRun:
         self.one_call = False              # True: steps use mp_update_step
         self.fold_last = True              # False: accumulate every micro-batch, then norm/AdamW
         self.device_weights = False        # True: weights from device counts, steps use the
-        self.dev_counts = None             # *_dw entry points (kept alive until the next step)
+        self.dev_counts = None             # group entry points (kept alive until the next step)
         self.dev_weights = None
         # (accumulate groups, folded group) of micro-batch indices: steps use
         # mp_accumulate_group per group, then mp_update_step_group on the folded one
@@ -182,8 +182,8 @@ class DeviceRun:
         return None
 
     def _step_device_weights(self, s, snapshot):
-        """The step with n_i in device memory: mp_token_weights_dev, mp_accumulate_dw and
-        mp_update_step_dw read the weights where the kernels run."""
+        """The step with n_i in device memory: mp_token_weights_dev, then the one-micro-batch
+        group calls, which read each weight where the kernels run."""
         torch, mp, w = self.torch, self.mp, self.w
         self.dev_counts = torch.tensor(w.token_counts(s), dtype=torch.int64, device="cuda")
         self.dev_weights = torch.empty(w.k, dtype=torch.float32, device="cuda")
@@ -191,14 +191,14 @@ class DeviceRun:
         wp = [self.dev_weights.data_ptr() + 4 * i for i in range(w.k)]
         n_acc = w.k if not self.fold_last else w.k - 1
         for i in range(n_acc):
-            mp.mp_accumulate_dw(self.model.plan, self.gsets[i], wp[i], i == 0)
+            mp.mp_accumulate_group(self.model.plan, [self.gsets[i]], wp[i], i == 0)
         acc_snapshot = ([a.cpu().numpy() for a in self.model.acc]
                         if snapshot and self.model.acc is not None else None)
         if not self.fold_last:
-            mp.mp_update_step_dw(self.model.plan, self.state, None, None, 0, w.max_norm, self.hp)
+            mp.mp_update_step(self.model.plan, self.state, None, 1.0, 0, w.max_norm, self.hp)
         else:
-            mp.mp_update_step_dw(self.model.plan, self.state, self.gsets[w.k - 1], wp[-1],
-                                 w.k == 1, w.max_norm, self.hp)
+            mp.mp_update_step_group(self.model.plan, self.state, [self.gsets[w.k - 1]], wp[-1],
+                                    w.k == 1, w.max_norm, self.hp)
         return acc_snapshot
 
     def host(self, name):

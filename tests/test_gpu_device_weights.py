@@ -2,9 +2,9 @@
 
 The weights of "Accumulate gradients and recompute activations", section "Weight each mean by
 the targets it represents", from counts that stay in device memory: mp_token_weights_dev must
-give the host call's bits, the *_dw entry points must step exactly as the host-weight ones do,
-counts the host would refuse must turn into a skipped step, and a captured graph must read the
-counts of each replay.
+give the host call's bits, the group entry points reading those weights on the device must step
+exactly as the host-weight calls do, counts the host would refuse must turn into a skipped step,
+and a captured graph must read the counts of each replay.
 """
 import sys
 
@@ -64,8 +64,9 @@ def test_refused_counts_give_nan_weights(mp):
 @pytest.mark.parametrize("name,fold_last", [("edges-fp16", True), ("llama-10.5M", True),
                                             ("edges", False)])
 def test_device_weight_steps_equal_the_oracle(mp, name, fold_last):
-    """Steps driven by mp_token_weights_dev, mp_accumulate_dw and mp_update_step_dw equal the
-    oracle's, through the fp16 list's overflow and change of S."""
+    """Steps driven by mp_token_weights_dev and one-micro-batch group calls reading the weights on
+    the device (mp_accumulate_group, mp_update_step_group) equal the oracle's, through the fp16
+    list's overflow and change of S."""
     from harness import OracleRun, DeviceRun, compare_step
     w = configs.make(name)
     orc = OracleRun(w)
@@ -102,9 +103,9 @@ def test_refused_counts_skip_the_step(mp):
         mp.mp_token_weights_dev(w.k, cnt, wts)
         plan = dev.model.plan
         for i in range(w.k - 1):
-            mp.mp_accumulate_dw(plan, dev.gsets[i], wts.data_ptr() + 4 * i, i == 0)
-        mp.mp_update_step_dw(plan, dev.state, dev.gsets[-1], wts.data_ptr() + 4 * (w.k - 1),
-                             w.k == 1, w.max_norm, dev.hp)
+            mp.mp_accumulate_group(plan, [dev.gsets[i]], wts.data_ptr() + 4 * i, i == 0)
+        mp.mp_update_step_group(plan, dev.state, [dev.gsets[-1]], wts.data_ptr() + 4 * (w.k - 1),
+                                w.k == 1, w.max_norm, dev.hp)
         after = dev.stats()
         say("  after refused counts:", after)
         assert after["found_inf"] == 1 and after["skipped"] == 1
@@ -142,9 +143,13 @@ def test_graph_replays_read_each_replays_counts(mp):
         plan = graphed.model.plan
         mp.mp_token_weights_dev(k, cnt, wts, st)
         for i in range(k - 1):
-            mp.mp_accumulate_dw(plan, graphed.gsets[i], wp[i], i == 0, st)
-        mp.mp_update_step_dw(plan, graphed.state, graphed.gsets[-1], wp[-1], 0, w.max_norm,
-                             graphed.hp, st)
+            mp.mp_accumulate_group(plan, [graphed.gsets[i]], wp[i], i == 0, st)
+        # the separate norm and AdamW calls, each reading the last weight on the device
+        mp.mp_unscale_check_norm_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0,
+                                       w.max_norm, st)
+        mp.mp_adamw_step_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0, graphed.hp,
+                               st)
+        mp.mp_scaler_update(graphed.state, st)
     try:
         for r in range(1, 5):
             counts = w.token_counts(r)

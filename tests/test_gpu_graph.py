@@ -78,8 +78,9 @@ def test_graph_replays_follow_the_scaler():
         plan = dev.model.plan
         mp.mp_token_weights_dev(k, cnt, wts, st)
         for i in range(k - 1):
-            mp.mp_accumulate_dw(plan, dev.gsets[i], wp[i], i == 0, st)
-        mp.mp_update_step_dw(plan, dev.state, dev.gsets[-1], wp[-1], 0, w.max_norm, dev.hp, st)
+            mp.mp_accumulate_group(plan, [dev.gsets[i]], wp[i], i == 0, st)
+        mp.mp_update_step_group(plan, dev.state, [dev.gsets[-1]], wp[-1], 0, w.max_norm, dev.hp,
+                                st)
     try:
         seen = set()
         for s in range(1, w.steps + 1):

@@ -165,11 +165,6 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_token_weights_dev(2, None, dev, None) == mp.MP_ERR_INVALID
     assert L.mp_token_weights_dev(2, ctypes.c_void_p(0x10004), dev, None) == mp.MP_ERR_ALIGN
     assert L.mp_token_weights_dev(2, dev, ctypes.c_void_p(0x10002), None) == mp.MP_ERR_ALIGN
-    assert L.mp_accumulate_dw(None, None, dev, 1, None) == mp.MP_ERR_INVALID
-    assert L.mp_accumulate_dw(fake_state, fake_state, None, 1, None) == mp.MP_ERR_INVALID
-    assert L.mp_update_step_dw(None, None, None, dev, 0, 1.0, None, None) == mp.MP_ERR_INVALID
-    assert (L.mp_update_step_dw(fake_state, fake_state, fake_state, None, 0, 1.0, None, None)
-            == mp.MP_ERR_INVALID)
     # group entry points: the group's size, NULL arrays and NULL members are refused first
     PP = ctypes.POINTER(ctypes.c_void_p)
     two = ctypes.cast((ctypes.c_void_p * 2)(0x10000, None), PP)
@@ -183,6 +178,14 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_accumulate_group(None, two, wts, 2, 0, 1, None) == mp.MP_ERR_INVALID
     assert (L.mp_update_step_group(None, None, two, wts, 2, 0, 1, 1.0, None, None)
             == mp.MP_ERR_INVALID)
+    for n in (0, 5):
+        assert (L.mp_unscale_check_norm_group(fake_state, fake_state, two, wts, n, 0, 0, 1.0, None)
+                == mp.MP_ERR_INVALID)
+        assert (L.mp_adamw_step_group(fake_state, fake_state, two, wts, n, 0, 0, None, None)
+                == mp.MP_ERR_INVALID)
+    assert L.mp_unscale_check_norm_group(None, None, two, wts, 2, 0, 0, 1.0, None) == mp.MP_ERR_INVALID
+    assert L.mp_adamw_step_group(None, None, two, wts, 2, 0, 0, None, None) == mp.MP_ERR_INVALID
+    assert L.mp_adamw_step_group(fake_state, fake_state, None, wts, 1, 0, 0, None, None) == mp.MP_ERR_INVALID
 
 
 def test_bench_refuses_more_than_one_gpu():
