@@ -1,8 +1,10 @@
-// One logical update through the C ABI of include/mpstep.h, with plain HIP
-// allocations and no framework: two micro-batches (the first accumulated, the
-// last folded in), then unscale/norm, AdamW and the scaler in one call.  The
-// inputs are chosen so that the results have closed forms, which the program
-// checks; it prints one line and exits 0 on success.
+// Two logical updates through the C ABI of include/mpstep.h, with plain HIP
+// allocations and no framework.  Step 1: two micro-batches (the first
+// accumulated, the last folded in), then unscale/norm, AdamW and the scaler in
+// one call.  Step 2: token weights computed on the device from device counts,
+// and both micro-batches folded into the norm and AdamW passes as one resident
+// group.  The inputs are chosen so that the results have closed forms, which
+// the program checks; it prints one line and exits 0 on success.
 //
 // Gradients are 2^-10 everywhere in both micro-batches, so with token counts
 // 3 and 1 the weighted sum 0.75 * 2^-10 + 0.25 * 2^-10 is exactly 2^-10, the
@@ -118,6 +120,38 @@ int main()
     }
     if (worst > 4 * std::ldexp(1.0, -25)) ++bad;        // a few fp32 ulps of 0.5
 
+    // Step 2, all on the device: target counts in device memory, token weights computed there,
+    // and both micro-batches, still resident, folded straight into the norm and AdamW passes
+    // (no accumulator pass).  The weights 1/4 and 3/4 of equal gradients sum to g exactly, so
+    // the sum of squares repeats, and with m, v bias-corrected the second step moves each
+    // weight by lr * g / (g + eps) again.
+    const int64_t counts2[2] = {1, 3};
+    int64_t* d_counts = nullptr;
+    float* d_weights = nullptr;
+    HIP_OK(hipMalloc(&d_counts, sizeof counts2));
+    HIP_OK(hipMalloc(&d_weights, 2 * sizeof(float)));
+    HIP_OK(hipMemcpy(d_counts, counts2, sizeof counts2, hipMemcpyHostToDevice));
+    const mp_gradset* both[2] = {set1, set2};
+    MP_OK_(mp_token_weights_dev(2, d_counts, d_weights, stream));
+    MP_OK_(mp_update_step_group(plan, state, both, d_weights, 2, 1, 1, 0.0f, &hp, stream));
+    mp_stats stats2;
+    MP_OK_(mp_state_read(state, &stats2, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    if (stats2.found_inf != 0 || stats2.step != 2 || stats2.sumsq != want_sumsq) ++bad;
+    const double want_w2 = master0 - 2e-3 * (g / (g + 1e-8));
+    double worst2 = 0.0;
+    for (int i = 0; i < n; ++i) {
+        std::vector<float> w(numel[i]);
+        HIP_OK(hipMemcpy(w.data(), master[i], numel[i] * sizeof(float), hipMemcpyDeviceToHost));
+        for (int64_t j = 0; j < numel[i]; ++j) {
+            const double err = std::fabs(static_cast<double>(w[j]) - want_w2);
+            worst2 = err > worst2 ? err : worst2;
+        }
+    }
+    if (worst2 > 8 * std::ldexp(1.0, -25)) ++bad;
+    (void)hipFree(d_counts);
+    (void)hipFree(d_weights);
+
     mp_gradset_destroy(set1);
     mp_gradset_destroy(set2);
     mp_state_destroy(state);
@@ -128,8 +162,8 @@ int main()
     (void)hipStreamDestroy(stream);
 
     std::printf("c_api_step: %s  params %lld  sumsq %.17g (want %.17g)  norm %.9g  "
-                "max |w - closed form| %.3g\n",
+                "max |w - closed form| %.3g after step 1, %.3g after step 2\n",
                 bad ? "MISMATCH" : "ok", static_cast<long long>(total), stats.sumsq, want_sumsq,
-                static_cast<double>(stats.grad_norm), worst);
+                static_cast<double>(stats.grad_norm), worst, worst2);
     return bad ? 1 : 0;
 }

@@ -1,6 +1,8 @@
 """The C ABI without PyTorch (needs a GPU): optimizer_step_tensor_amd/examples/c_api_step,
-a plain HIP program built by __graft_entry__.build(), runs one update on hipMalloc'd buffers
-and checks it against closed forms (exact sum of squares, first AdamW step)."""
+a plain HIP program built by __graft_entry__.build(), runs two updates on hipMalloc'd buffers
+(the second with token weights computed on the device and both micro-batches folded in as one
+group) and checks them against closed forms (exact sum of squares, the first two AdamW
+steps)."""
 import os
 import subprocess
 
