@@ -219,9 +219,8 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=
     - saving and restoring the device state (scaler and optimizer clock);
     - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
       multiples of 64 elements), its accumulate passes, partial norm + finish, AdamW, scaler;
-    - the step with k <= 4 micro-batch gradients resident, folded in groups: two accumulated in
-      one pass and two folded into the norm and AdamW passes, or all k folded there (no
-      accumulator pass at all).  Same results, bit for bit, as the timed step."""
+    - the step with all k micro-batch gradients resident, folded in groups of up to four
+      (time_groups).  Same results, bit for bit, as the timed step."""
     def want(name):
         return only is None or name in only
 
@@ -243,7 +242,7 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=
         out["state_save_restore"] = time_save_restore(mp, torch, state, stream)
     if want("zero8_rank_share"):
         out["zero8_rank_share"] = time_rank_share(mp, torch, w, model, g16, hp, weights, stream)
-    if want("resident_groups") and 2 <= w.k <= 4:
+    if want("resident_groups") and w.k >= 2:
         out["resident_groups"] = time_groups(mp, torch, w, model, sets, state, hp, weights,
                                              stream)
     return out
@@ -317,10 +316,19 @@ def group_bytes_per_param(acc_groups, fold):
 
 
 def time_groups(mp, torch, w, model, sets, state, hp, weights, stream, reps=3):
+    """k <= 4: all micro-batches folded into the norm and AdamW passes, and (k >= 3) the first
+    two accumulated in one pass with the rest folded.  k > 4: the first k - 4 accumulated in
+    groups of up to four, the last four folded."""
     k = w.k
-    schedules = {"all_folded": ([], list(range(k)))}
-    if k >= 3:
-        schedules["two_accumulated"] = ([[0, 1]], list(range(2, k)))
+    schedules = {}
+    if k <= 4:
+        schedules["all_folded"] = ([], list(range(k)))
+        if k >= 3:
+            schedules["two_accumulated"] = ([[0, 1]], list(range(2, k)))
+    else:
+        head = list(range(k - 4))
+        schedules["groups_of_four"] = ([head[i:i + 4] for i in range(0, len(head), 4)],
+                                       list(range(k - 4, k)))
     out = {}
     for name, (acc_groups, fold) in schedules.items():
         def step():
