@@ -29,19 +29,32 @@ def test_full_size_sampled_parity(name, steps):
 
 
 @pytest.mark.timeout(1100)
+@pytest.mark.parametrize("name,schedule", [
+    ("llama3-8B", ([], [0, 1, 2, 3])),              # all four resident, no accumulator pass
+    ("gpt-1.3B", ([[0, 1, 2, 3]], [4, 5, 6, 7])),   # four accumulated in one pass, four folded
+])
+def test_full_size_resident_groups(name, schedule):
+    """The group schedules bench.py times (extras.resident_groups), at full size, against the
+    oracle's one-at-a-time steps on the same sampled windows and the full streamed norm."""
+    run_sampled_parity(name, 2, schedule=schedule)
+
+
+@pytest.mark.timeout(1100)
 @pytest.mark.skipif(os.environ.get("MPSTEP_LONG") != "1",
                     reason="the 1.3B list's 20-step run takes about 3 minutes; MPSTEP_LONG=1 runs it")
 def test_full_size_gpt13b_twenty_steps():
     run_sampled_parity("gpt-1.3B", 20)
 
 
-def run_sampled_parity(name, steps):
+def run_sampled_parity(name, steps, schedule=None):
     import torch
     from harness import DeviceRun, StreamedOracle, sample_windows, compare_windows
     assert torch.cuda.is_available()
     w = configs.make(name)
-    say("full-size %s: %d tensors, %d params, k=%d" % (name, len(w.tensors), w.total, w.k))
+    say("full-size %s: %d tensors, %d params, k=%d, schedule %s"
+        % (name, len(w.tensors), w.total, w.k, schedule))
     dev = DeviceRun(w, layout="flat")
+    dev.schedule = schedule
     so = StreamedOracle(w, sample_windows(w), log=say)
     try:
         for s in range(1, steps + 1):
