@@ -100,3 +100,51 @@ def test_graph_replays_follow_the_scaler():
     finally:
         del g
         dev.close()
+
+
+def test_graph_replays_of_a_resident_group_step():
+    """A captured step that folds all four resident micro-batches into the norm and AdamW passes
+    (no accumulator pass), with the weights computed on the device from a count buffer rewritten
+    between replays, equals the same group step run eagerly with host weights, bit for bit, on
+    every replay."""
+    import numpy as np
+    import torch
+    import optimizer_step_tensor_amd as mp
+    from harness import DeviceRun
+    w = configs.make("llama-10.5M")
+    eager, graphed = DeviceRun(w), DeviceRun(w)
+    k = w.k
+    cnt = torch.ones(k, dtype=torch.int64, device="cuda")
+    wts = torch.empty(k, dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        st = torch.cuda.current_stream()
+        mp.mp_token_weights_dev(k, cnt, wts, st)
+        mp.mp_update_step_group(graphed.model.plan, graphed.state, graphed.gsets, wts, 1,
+                                w.max_norm, graphed.hp, st)
+    try:
+        for r in range(1, 5):
+            counts = w.token_counts(r)
+            eager.fill_grads(r, 1.0)
+            graphed.fill_grads(r, 1.0)
+            cnt.copy_(torch.tensor(counts, dtype=torch.int64))
+            torch.cuda.synchronize()
+            mp.mp_update_step_group(eager.model.plan, eager.state, eager.gsets,
+                                    mp.mp_token_weights(counts), 1, w.max_norm, eager.hp)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(wts.cpu().numpy(),
+                                  np.array(mp.mp_token_weights(counts), np.float32)), r
+            a, b = eager.stats(), graphed.stats()
+            assert a == b and a["step"] == r
+            for name in ("master", "m", "v"):
+                for x, y in zip(getattr(eager.model, name), getattr(graphed.model, name)):
+                    assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (r, name)
+            for x, y in zip(eager.model.w16, graphed.model.w16):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (r, "w16")
+    finally:
+        del g
+        eager.close()
+        graphed.close()
