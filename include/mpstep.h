@@ -364,6 +364,14 @@ mp_status mp_adamw_step_group(mp_plan* plan, mp_state* state, const mp_gradset* 
                               const float* weights, int32_t n, int32_t weights_on_device,
                               int32_t last_is_first, const mp_adamw_hparams* hp, mp_stream stream);
 
+/* mp_norm_partial over a group of resident micro-batches, for a sharded model
+ * (ZeRO-1/2) whose ranks fold their micro-batches in groups: the partial sum
+ * of squares of the same gradient mp_unscale_check_norm_group measures.  Then
+ * mp_norm_finish, and mp_adamw_step_group with the same group. */
+mp_status mp_norm_partial_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,
+                                const float* weights, int32_t n, int32_t weights_on_device,
+                                int32_t last_is_first, double* partial_out, mp_stream stream);
+
 /* Elementwise casts with the step's conversions: dst = round-to-nearest-even
  * of src into the 16-bit format (as in mp_adamw_step), and dst = exact fp32
  * value of a 16-bit pattern (as in mp_accumulate).  Useful to initialise the

@@ -33,6 +33,7 @@ ENTRY_POINTS = [
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
     "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_group",
     "mp_update_step_group", "mp_unscale_check_norm_group", "mp_adamw_step_group",
+    "mp_norm_partial_group",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -126,6 +127,7 @@ def _bind(L):
         "mp_unscale_check_norm_group": ([P, P, PP, P, i32, i32, i32, f32, P], i32),
         "mp_adamw_step_group": ([P, P, PP, P, i32, i32, i32, ctypes.POINTER(AdamWHparams), P],
                                 i32),
+        "mp_norm_partial_group": ([P, P, PP, P, i32, i32, i32, P, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -320,6 +322,13 @@ def mp_unscale_check_norm_group(plan, state, sets, weights, last_is_first, max_n
     _check(lib().mp_unscale_check_norm_group(plan, state, arr, w, len(sets), dev,
                                              int(bool(last_is_first)), float(max_norm),
                                              _stream(stream)))
+
+
+def mp_norm_partial_group(plan, state, sets, weights, last_is_first, partial_out, stream=None):
+    arr, w, dev = _group(sets, weights)
+    _check(lib().mp_norm_partial_group(plan, state, arr, w, len(sets), dev,
+                                       int(bool(last_is_first)), _addr(partial_out),
+                                       _stream(stream)))
 
 
 def mp_adamw_step_group(plan, state, sets, weights, last_is_first, hp, stream=None):

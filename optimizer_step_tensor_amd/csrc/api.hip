@@ -863,13 +863,14 @@ mp_status mp_unscale_check_norm(mp_plan* plan, mp_state* state, const mp_gradset
                               max_norm, stream);
 }
 
-mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
-                          int32_t last_is_first, double* partial_out, mp_stream stream)
+namespace {
+
+mp_status norm_partial(mp_plan* plan, mp_state* state, const Group& g, double* partial_out,
+                       mp_stream stream)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     if (partial_out == nullptr || (reinterpret_cast<uintptr_t>(partial_out) & 7u) != 0)
         return fail(MP_ERR_INVALID, "partial_out must be an 8-byte aligned device pointer");
-    const Group g = single(last, host_weight(w_last), last_is_first);
     mp_status st = check_group(plan, g);
     if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
@@ -882,6 +883,25 @@ mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last
     plan->norm_state = state;
     plan->norm_group = g;
     return ok();
+}
+
+}  // namespace
+
+mp_status mp_norm_partial(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
+                          int32_t last_is_first, double* partial_out, mp_stream stream)
+{
+    return norm_partial(plan, state, single(last, host_weight(w_last), last_is_first),
+                        partial_out, stream);
+}
+
+mp_status mp_norm_partial_group(mp_plan* plan, mp_state* state, const mp_gradset* const* sets,
+                                const float* weights, int32_t n, int32_t weights_on_device,
+                                int32_t last_is_first, double* partial_out, mp_stream stream)
+{
+    Group g;
+    mp_status st = make_group(sets, weights, n, weights_on_device, last_is_first, &g);
+    if (st != MP_OK) return st;
+    return norm_partial(plan, state, g, partial_out, stream);
 }
 
 mp_status mp_norm_finish(mp_plan* plan, mp_state* state, const double* sumsq, float max_norm,

@@ -83,6 +83,18 @@ def test_sharded_norm_matches_unsharded(mp, name):
     """'Megatron Internals III' sections 6 and 9 / 'Your weights fit...' (ZeRO): four ranks' slices,
     each with its own plan and state replica; one reduction of the partial sums of squares gives
     every rank the global norm and the same skip decision; the result is the unsharded update."""
+    run_sharded(mp, name, grouped=False)
+
+
+@pytest.mark.parametrize("name", ["edges-fp16", "llama-10.5M"])
+def test_sharded_norm_with_resident_groups(mp, name):
+    """The same four ranks, each folding all of its resident micro-batches into the partial norm
+    and the AdamW pass as one group (mp_norm_partial_group, mp_adamw_step_group): still the
+    unsharded one-at-a-time update, bit for bit, through the fp16 list's overflow."""
+    run_sharded(mp, name, grouped=True)
+
+
+def run_sharded(mp, name, grouped):
     import torch
     from harness import OracleRun, DeviceRun, compare_step
     w = configs.make(name)
@@ -102,6 +114,10 @@ def test_sharded_norm_matches_unsharded(mp, name):
             dev.fill_grads(s, scale)
             wts = mp.mp_token_weights(w.token_counts(s))
             for r, (plan, sets) in enumerate(plans):
+                if grouped:
+                    mp.mp_norm_partial_group(plan, states[r], sets, wts, 1,
+                                             partials.data_ptr() + 8 * r)
+                    continue
                 for i in range(w.k - 1):
                     mp.mp_accumulate(plan, sets[i], wts[i], i == 0)
                 mp.mp_norm_partial(plan, states[r], sets[-1], wts[-1], 0,
@@ -114,7 +130,10 @@ def test_sharded_norm_matches_unsharded(mp, name):
             total.fill_(acc_sum)
             for r, (plan, sets) in enumerate(plans):
                 mp.mp_norm_finish(plan, states[r], total.data_ptr(), w.max_norm)
-                mp.mp_adamw_step(plan, states[r], sets[-1], wts[-1], 0, dev.hp)
+                if grouped:
+                    mp.mp_adamw_step_group(plan, states[r], sets, wts, 1, dev.hp)
+                else:
+                    mp.mp_adamw_step(plan, states[r], sets[-1], wts[-1], 0, dev.hp)
                 mp.mp_scaler_update(states[r])
             # every rank holds the same scalars; compare the full tensors with the oracle
             stats = [mp.read_stats(st) for st in states]

@@ -186,6 +186,11 @@ def test_validation_before_any_device_work(mp):
     assert L.mp_unscale_check_norm_group(None, None, two, wts, 2, 0, 0, 1.0, None) == mp.MP_ERR_INVALID
     assert L.mp_adamw_step_group(None, None, two, wts, 2, 0, 0, None, None) == mp.MP_ERR_INVALID
     assert L.mp_adamw_step_group(fake_state, fake_state, None, wts, 1, 0, 0, None, None) == mp.MP_ERR_INVALID
+    for n in (0, 5):
+        assert (L.mp_norm_partial_group(fake_state, fake_state, two, wts, n, 0, 0,
+                                        ctypes.c_void_p(0x10000), None) == mp.MP_ERR_INVALID)
+    assert (L.mp_norm_partial_group(None, None, two, wts, 1, 0, 0, ctypes.c_void_p(0x10000), None)
+            == mp.MP_ERR_INVALID)
 
 
 def test_bench_refuses_more_than_one_gpu():
