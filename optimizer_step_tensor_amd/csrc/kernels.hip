@@ -438,10 +438,30 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
     return sign | static_cast<uint32_t>(m);
 }
 
+// The codes of x[0..3] / scale.  The quotients go through gfx950's fp32 -> fp8
+// pack instruction, which rounds to nearest even into E4M3 exactly as e4m3_code
+// does for every finite input below 464 in magnitude (subnormals and zeros
+// included); it was compared with e4m3_code on all 2^32 fp32 patterns.  At and
+// above 464, for infinities and for NaN it returns a NaN code instead, so those
+// quotients take e4m3_code (saturation to 448, NaN with its sign).  A block's
+// quotients stay at or below 448 unless its maximum is infinite or NaN.
 __device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
 {
-    return e4m3_code(x.v[0] / scale) | (e4m3_code(x.v[1] / scale) << 8) |
-           (e4m3_code(x.v[2] / scale) << 16) | (e4m3_code(x.v[3] / scale) << 24);
+    float q[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) q[k] = x.v[k] / scale;
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    uint32_t packed = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true));
+    bool special = false;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) special |= (__float_as_uint(q[k]) & 0x7FFFFFFFu) >= 0x43E80000u;
+    if (special) {
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k)
+            if ((__float_as_uint(q[k]) & 0x7FFFFFFFu) >= 0x43E80000u)
+                packed = (packed & ~(0xFFu << (8 * k))) | (e4m3_code(q[k]) << (8 * k));
+    }
+    return packed;
 }
 
 // Scale of the 16-value block held by lanes 4q..4q+3 (4 consecutive values
