@@ -330,7 +330,9 @@ mp_status mp_scaler_update(mp_state* state, mp_stream stream);
  * mp_adamw_step and mp_scaler_update with the same arguments, enqueued in that
  * order on `stream` -- the scaler's step of "Mixed precision ...", section 4
  * "The interface" (check, unscale, clip, optimizer step, update S).  Every
- * structural check of the three calls is made before anything is enqueued. */
+ * structural check of the three calls is made before anything is enqueued.
+ * The optimizer clock and the scaler's decision share one tiny launch here,
+ * since nothing can run between them. */
 mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last, float w_last,
                          int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
                          mp_stream stream);

@@ -786,7 +786,7 @@ mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, flo
 }
 
 mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_adamw_hparams* hp,
-                     const Fp8Out* fp8, mp_stream stream)
+                     const Fp8Out* fp8, mp_stream stream, bool with_scaler = false)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     mp_status st = check_hparams(hp);
@@ -800,9 +800,10 @@ mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_ad
     if (st != MP_OK) return st;
     mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
     hipError_t e = mpk::launch_adamw(view(plan), plan->grid, device_group(g), plan->dtype, a, fp8,
-                                     state->d, static_cast<hipStream_t>(stream));
+                                     state->d, with_scaler, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "adamw launch");
     plan->norm_pending = false;
+    if (with_scaler) state->decision_pending = false;   // the decision ran in the same launch
     return ok();
 }
 
@@ -818,8 +819,7 @@ mp_status update_step(mp_plan* plan, mp_state* state, const Group& g, float max_
     if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
     st = unscale_check_norm(plan, state, g, max_norm, stream);
-    if (st == MP_OK) st = adamw_step(plan, state, g, hp, nullptr, stream);
-    if (st == MP_OK) st = mp_scaler_update(state, stream);
+    if (st == MP_OK) st = adamw_step(plan, state, g, hp, nullptr, stream, true);
     return st;
 }
 

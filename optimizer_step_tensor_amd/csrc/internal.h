@@ -135,8 +135,9 @@ hipError_t launch_norm(const PlanView& p, int grid, const Grads& g, int dtype, d
 hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int dtype,
                                double* partials, const DevState* st, double* out, hipStream_t s);
 hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s);
+// with_scaler: the scaler's decision runs in the same tiny launch as the clock
 hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, const AdamArgs& a,
-                        const Fp8Out* fp8, DevState* st, hipStream_t s);
+                        const Fp8Out* fp8, DevState* st, bool with_scaler, hipStream_t s);
 hipError_t launch_scaler(DevState* st, hipStream_t s);
 hipError_t launch_token_weights(const int64_t* counts, int k, float* weights, hipStream_t s);
 hipError_t launch_cast_to_16(const float* src, uint16_t* dst, int64_t n, int dtype, hipStream_t s);

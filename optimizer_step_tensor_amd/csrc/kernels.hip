@@ -598,9 +598,9 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
 
 // The optimizer clock advances only on a committed step ("Accumulate gradients
 // and recompute activations", "Discard a failed partial logical update").
-__global__ void k_adam_clock(DevState* __restrict__ st, float beta1, float beta2)
+__device__ void advance_clock(DevState* __restrict__ st, float beta1, float beta2)
 {
-    if (threadIdx.x != 0 || st->s.found_inf) return;
+    if (st->s.found_inf) return;
     st->s.step += 1;
     st->s.beta1_pow = st->s.beta1_pow * static_cast<double>(beta1);
     st->s.beta2_pow = st->s.beta2_pow * static_cast<double>(beta2);
@@ -608,9 +608,8 @@ __global__ void k_adam_clock(DevState* __restrict__ st, float beta1, float beta2
 
 // Dynamic loss-scale controller ("Mixed precision ...", section 2 "Dynamic
 // scaling"; "Megatron Internals III", section 5).
-__global__ void k_scaler(DevState* __restrict__ st)
+__device__ void scaler_decision(DevState* __restrict__ st)
 {
-    if (threadIdx.x != 0) return;
     const int found_inf = st->s.found_inf;
     st->s.skipped = found_inf;
     if (found_inf) st->s.skipped_total += 1;
@@ -631,6 +630,25 @@ __global__ void k_scaler(DevState* __restrict__ st)
     }
     st->s.scale = scale;
     st->inv_scale = 1.0f / scale;
+}
+
+__global__ void k_adam_clock(DevState* __restrict__ st, float beta1, float beta2)
+{
+    if (threadIdx.x == 0) advance_clock(st, beta1, beta2);
+}
+
+__global__ void k_scaler(DevState* __restrict__ st)
+{
+    if (threadIdx.x == 0) scaler_decision(st);
+}
+
+// Both, in that order, in one launch: the tail of a whole update enqueued by one
+// call, where nothing can run between them.
+__global__ void k_clock_scaler(DevState* __restrict__ st, float beta1, float beta2)
+{
+    if (threadIdx.x != 0) return;
+    advance_clock(st, beta1, beta2);
+    scaler_decision(st);
 }
 
 // Token weights on the device ("Accumulate gradients and recompute activations",
@@ -858,7 +876,7 @@ hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, 
 }
 
 hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, const AdamArgs& a,
-                        const Fp8Out* fp8, DevState* st, hipStream_t s)
+                        const Fp8Out* fp8, DevState* st, bool with_scaler, hipStream_t s)
 {
     hipError_t err;
     if (fp8 != nullptr) {
@@ -876,7 +894,8 @@ hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, 
         });
     }
     if (err != hipSuccess) return err;
-    k_adam_clock<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
+    if (with_scaler) k_clock_scaler<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
+    else             k_adam_clock<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
     return hipGetLastError();
 }
 
