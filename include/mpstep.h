@@ -269,9 +269,11 @@ mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, cons
  * (last_is_first != 0), or fl(acc + fl(w_last * widen(last))) -- the last
  * micro-batch folded in exactly as mp_accumulate would add it.  Then
  *   g = fl(g_eff * (1/S));  found_inf = any g is inf or NaN;
- *   sumsq = sum g^2 in binary64 (a fixed-order reduction: per chunk, then
- *           256 contiguous range sums, then one total; the same bits on
- *           every run);  grad_norm = fp32(sqrt(sumsq));
+ *   sumsq = sum g^2 in binary64 (a fixed-order reduction: per block of
+ *           chunks -- one chunk, or eight when the pass reads a single
+ *           16-bit stream and no accumulator -- then 256 contiguous range
+ *           sums, then one total; the same bits on every run);
+ *   grad_norm = fp32(sqrt(sumsq));
  *   clip_coef = min(1, fl(max_norm / fl(grad_norm + 1e-6))) if max_norm > 0
  *               and !found_inf, else 1.
  * Results stay on the device for mp_adamw_step and mp_state_read. */
