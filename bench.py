@@ -420,6 +420,8 @@ def main():
     # every pass reads its weight there: the whole step is stream-ordered device work
     counts_dev = torch.tensor(counts, dtype=torch.int64, device="cuda")
     weights_dev = torch.empty(k, dtype=torch.float32, device="cuda")
+    # the timed loop calls the C ABI directly with arguments marshalled once here, so no
+    # per-call ctypes array building lands in the step time of the small workloads
     L = mp.lib()
     PP = ctypes.POINTER(ctypes.c_void_p)
     one = [ctypes.cast((ctypes.c_void_p * 1)(x.value), PP) for x in sets]   # groups of one
