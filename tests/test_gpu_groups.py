@@ -186,3 +186,52 @@ def test_group_argument_errors(mp):
             mp.mp_gradset_destroy(x)
         mp.mp_state_destroy(state)
         m.close()
+
+
+def test_group_with_refused_device_counts_skips(mp):
+    """A resident group whose device weights come from counts the host call would refuse (a
+    micro-batch without targets) folds NaN weights in, so the step overflows and is skipped:
+    nothing written, the clock kept, S backed off."""
+    import torch
+    from harness import DeviceRun
+    w = configs.make("edges-fp16")
+    dev = DeviceRun(w)
+    try:
+        dev.fill_grads(1, w.scaler["init_scale"])
+        before = dev.stats()
+        snap = [x.clone() for x in dev.model.master]
+        cnt = torch.tensor([5] * (w.k - 1) + [0], dtype=torch.int64, device="cuda")
+        wts = torch.empty(w.k, dtype=torch.float32, device="cuda")
+        mp.mp_token_weights_dev(w.k, cnt, wts)
+        mp.mp_update_step_group(dev.model.plan, dev.state, dev.gsets, wts, True, w.max_norm,
+                                dev.hp)
+        after = dev.stats()
+        assert after["found_inf"] == 1 and after["skipped"] == 1 and after["step"] == 0
+        assert after["scale"] == before["scale"] * w.scaler["backoff"]
+        for x, y in zip(snap, dev.model.master):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    finally:
+        dev.close()
+
+
+def test_group_with_a_repeated_micro_batch(mp):
+    """A gradset may appear twice in a group: the fold adds it twice, exactly as two
+    one-by-one accumulations of it do."""
+    import torch
+    from harness import DeviceRun
+    w = configs.make("edges")
+    a, b = DeviceRun(w), DeviceRun(w)
+    try:
+        for run in (a, b):
+            run.fill_grads(1, 1.0)
+        mp.mp_accumulate_group(a.model.plan, [a.gsets[0], a.gsets[1], a.gsets[0]],
+                               [0.25, 0.5, 0.25], True)
+        mp.mp_accumulate(b.model.plan, b.gsets[0], 0.25, True)
+        mp.mp_accumulate(b.model.plan, b.gsets[1], 0.5, False)
+        mp.mp_accumulate(b.model.plan, b.gsets[0], 0.25, False)
+        torch.cuda.synchronize()
+        for x, y in zip(a.model.acc, b.model.acc):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    finally:
+        a.close()
+        b.close()
