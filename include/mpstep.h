@@ -270,7 +270,7 @@ mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, cons
  * micro-batch folded in exactly as mp_accumulate would add it.  Then
  *   g = fl(g_eff * (1/S));  found_inf = any g is inf or NaN;
  *   sumsq = sum g^2 in binary64 (a fixed-order reduction: per block of
- *           chunks -- one chunk, or eight when the pass reads a single
+ *           chunks -- one chunk, or sixteen when the pass reads a single
  *           16-bit stream and no accumulator -- then 256 contiguous range
  *           sums, then one total; the same bits on every run);
  *   grad_norm = fp32(sqrt(sumsq));

@@ -55,7 +55,7 @@ constexpr int kBlock = 256;                          // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
 constexpr int kXcds = 8;                             // XCDs per MI355X
 constexpr int kNormStage2 = 256;                     // second-stage sums of the norm
-constexpr int kNormChunks16 = 8;                     // chunks per norm block, one 16-bit stream
+constexpr int kNormChunks16 = 16;                    // chunks per norm block, one 16-bit stream
 constexpr int kGroup = 4;                            // elements per 16-byte fp32 vector
 constexpr int kGroupsPerLane = MPK_GROUPS_PER_LANE;
 constexpr int kWaveSlab = kWave * kGroup * kGroupsPerLane;   // 512 elements per wave pass

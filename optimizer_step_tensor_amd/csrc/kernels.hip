@@ -812,8 +812,8 @@ hipError_t with_group(int dtype, const Grads& g, Fn&& fn)
 
 // First stage of the norm.  One block per chunk, except when the pass reads a
 // single 16-bit stream (one micro-batch, no accumulator): a chunk is then only
-// 4 KiB, and giving each block kNormChunks16 chunks (32 KiB) made the pass 28-37%
-// faster on the 124M, ragged, 1.3B and 8B lists (timed against 1 and 4 chunks).
+// 4 KiB, and giving each block kNormChunks16 chunks (64 KiB) made the pass 30-38%
+// faster on the 124M, ragged, 1.3B and 8B lists (timed against 1, 4, 8 and 32).
 // With two 16-bit streams the lists disagreed (8B faster with 4 chunks, 1.3B
 // slower), and from 6 bytes per element up one chunk per block was fastest.
 // *used: the blocks launched, i.e. the number of first-stage partials.
