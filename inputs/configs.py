@@ -168,6 +168,12 @@ def make(name):
         # one tensor past 2^31 elements (element offsets that need 64 bits everywhere: chunk
         # starts, pointers, generator indices) next to a tiny one; bf16, k = 2
         return Workload(20, name, [("big", (2 ** 31 + 4097,)), ("small", (7,))], BF16, 2, steps=2)
+    if name == "edges-k1":
+        # the bf16 edge list with one micro-batch: no accumulator, so the norm reads the 16-bit
+        # gradient alone and its blocks each walk several ragged chunks
+        sizes = [1, 2, 3, 4, 5, 7, 8, 9, 255, 256, 257, 511, 512, 513, 2047, 2048, 2049, 4095,
+                 4096, 4097, 65535, 65536, 65537, 1000003]
+        return Workload(21, name, [("k%02d" % i, (n,)) for i, n in enumerate(sizes)], BF16, 1)
     if name == "gpt-124M-scaler":
         # the fp16 run's scaler, overflow and gradient recipe on a small tensor list, long enough
         # for the scale to grow back: 2000 clean steps after the overflow of step 3

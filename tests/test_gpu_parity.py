@@ -125,6 +125,24 @@ def test_workload_parity(mp, name):
         dev.close()
 
 
+def test_one_micro_batch_on_the_edge_list(mp):
+    """One bf16 micro-batch, no accumulator, on the ragged edge list (sizes 1..1000003): the
+    norm pass reads the 16-bit gradient alone, each of its blocks walking 16 ragged chunks,
+    and every step equals the oracle."""
+    from harness import OracleRun, DeviceRun, compare_step
+    w = configs.make("edges-k1")
+    orc = OracleRun(w)
+    dev = DeviceRun(w)
+    try:
+        for s in range(1, w.steps + 1):
+            scale = orc.st.scaler.scale
+            orc.step()
+            dev.step(scale)
+            say("  step", s, compare_step(dev, orc, w, s))
+    finally:
+        dev.close()
+
+
 @pytest.mark.parametrize("name", ["edges-fp16", "llama-10.5M"])
 def test_update_step_in_one_call(mp, name):
     """mp_update_step (unscale/check/norm, AdamW, scaler in one call) equals the oracle as the
