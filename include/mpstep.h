@@ -200,7 +200,10 @@ mp_status mp_gradset_destroy(mp_gradset* set);
  * ones.  Before rewriting a slot the call waits until the copy that last read
  * it has run, so the host can run at most 4 updates ahead of the device.
  * Refused (MP_ERR_INVALID) while `stream` is being captured into a graph: a
- * replay would copy whatever the slot holds at replay time. */
+ * replay would copy whatever the slot holds at replay time.  A norm measured
+ * (mp_unscale_check_norm, mp_norm_partial and their group forms) with this
+ * gradset folded in no longer describes it: the AdamW step that would follow
+ * returns MP_ERR_ORDER until the norm is measured again. */
 mp_status mp_gradset_update(mp_gradset* set, void* const* g16, mp_stream stream);
 
 /* Device state: S = init_scale, no good steps, t = 0, beta powers 1. */
@@ -389,11 +392,14 @@ mp_status mp_widen_16(const uint16_t* src, float* dst, int64_t n, mp_dtype16 dty
  * listing 41.5), e.g. of the updated fp32 masters for an FP8 forward pass.
  * For each block of `block` consecutive values (block a multiple of 16 in
  * [16, 1024]; n a multiple of block, else MP_ERR_INVALID):
- *   scales[b] = fl(max|x| / 448), or 1 for an all-zero block (NaNs are
- *   ignored by the maximum);
+ *   scales[b] = fl(max|x| / 448), or 1 for an all-zero block; the maximum
+ *   propagates NaN as the listing's NumPy maximum does, so a block holding a
+ *   NaN gets the quiet NaN 0x7FC00000 as its scale;
  *   codes[i]  = E4M3(fl(x_i / scales[b])): 1 sign, 4 exponent bits (bias 7),
  *   3 mantissa bits, round to nearest even, saturating at 448 (E4M3 has no
- *   infinity), NaN -> S.1111.111.
+ *   infinity), NaN -> S.1111.111.  A NaN quotient (every value of a NaN-scale
+ *   block, or inf / inf in a block whose maximum is infinite) takes the sign
+ *   bit of x_i, IEEE 754 leaving the sign of a NaN result open.
  * Dequantisation is value(codes[i]) * scales[b].  src and codes 16-byte
  * aligned, scales 4-byte aligned; n/block scales are written. */
 mp_status mp_cast_fp8_blocks(const float* src, uint8_t* codes, float* scales, int64_t n,

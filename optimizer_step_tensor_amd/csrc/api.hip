@@ -45,6 +45,7 @@ struct mp_plan {
     bool norm_pending;
     const mp_state* norm_state;
     Group norm_group;         // the micro-batches the pending norm folded in
+    uint64_t norm_gen[mpk::kMaxGroup];   // their gradsets' generations at that time
     std::vector<int64_t> numel;  // per tensor, for validating FP8 output sets
 };
 
@@ -59,6 +60,9 @@ struct mp_gradset {
     uint16_t** h_slots[kGradsetSlots];
     hipEvent_t copied[kGradsetSlots];
     int next_slot;
+    // bumped by every mp_gradset_update: a norm measured before it folded in
+    // other buffers, so the AdamW step that would fold in these is refused
+    uint64_t generation;
 };
 
 struct mp_fp8set {
@@ -258,6 +262,23 @@ bool same_group(const Group& a, const Group& b)
     if (a.n != b.n || a.no_acc != b.no_acc) return false;
     for (int i = 0; i < a.n; ++i)
         if (a.sets[i] != b.sets[i] || !same_weight(a.w[i], b.w[i])) return false;
+    return true;
+}
+
+// The group a pending norm measured, with its gradsets' generations.
+void remember_norm_group(mp_plan* plan, const Group& g)
+{
+    plan->norm_group = g;
+    for (int i = 0; i < g.n; ++i) plan->norm_gen[i] = g.sets[i]->generation;
+}
+
+// g is the group the pending norm measured and none of its gradsets has been
+// pointed at other buffers since.
+bool norm_measured(const mp_plan* plan, const Group& g)
+{
+    if (!same_group(plan->norm_group, g)) return false;
+    for (int i = 0; i < g.n; ++i)
+        if (g.sets[i]->generation != plan->norm_gen[i]) return false;
     return true;
 }
 
@@ -556,6 +577,7 @@ mp_status mp_gradset_update(mp_gradset* set, void* const* g16, mp_stream stream)
         if (e == hipSuccess) e = hipEventRecord(set->copied[slot], s);
         if (e != hipSuccess) return hip_fail(e, "gradset update");
         set->next_slot = (slot + 1) % kGradsetSlots;
+        set->generation += 1;
         return ok();
     });
 }
@@ -781,7 +803,7 @@ mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, flo
     plan->partial_pending = false;
     plan->norm_pending = true;
     plan->norm_state = state;
-    plan->norm_group = g;
+    remember_norm_group(plan, g);
     return ok();
 }
 
@@ -793,9 +815,10 @@ mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_ad
     if (st != MP_OK) return st;
     st = check_group(plan, g);
     if (st != MP_OK) return st;
-    if (!plan->norm_pending || plan->norm_state != state || !same_group(plan->norm_group, g))
+    if (!plan->norm_pending || plan->norm_state != state || !norm_measured(plan, g))
         return fail(MP_ERR_ORDER, "the AdamW step must follow mp_unscale_check_norm on the same "
-                                  "plan and state, with the same last micro-batch arguments");
+                                  "plan and state, with the same last micro-batch arguments and "
+                                  "no mp_gradset_update of them in between");
     st = check_devices(plan, state);
     if (st != MP_OK) return st;
     mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
@@ -881,7 +904,7 @@ mp_status norm_partial(mp_plan* plan, mp_state* state, const Group& g, double* p
     plan->partial_pending = true;
     plan->norm_pending = false;
     plan->norm_state = state;
-    plan->norm_group = g;
+    remember_norm_group(plan, g);
     return ok();
 }
 

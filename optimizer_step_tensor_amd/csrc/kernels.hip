@@ -418,8 +418,26 @@ __global__ void k_norm_apply(const double* __restrict__ sumsq, float max_norm,
 // Fine-grained FP8 ("Chapter 41 Training at Scale", section 41.5): blocks of
 // consecutive values; scale = max|x| / 448 (a zero block takes 1); each value
 // x / scale rounded to E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no
-// infinity: saturate at 448; NaN -> S.1111.111).
+// infinity: saturate at 448; NaN -> S.1111.111).  The maximum propagates NaN
+// as the section's NumPy maximum does: a block holding a NaN gets the quiet
+// NaN 0x7FC00000 as its scale and the NaN code for every value.  A NaN
+// quotient (NaN scale, or inf / inf) takes the sign bit of its value.
 // ---------------------------------------------------------------------------
+constexpr uint32_t kQuietNan = 0x7FC00000u;
+
+// max(amax, a) for the block maximum: a NaN wins, and stays.
+__device__ __forceinline__ float nan_max(float amax, float a)
+{
+    return (a > amax || a != a) ? a : amax;
+}
+
+__device__ __forceinline__ float block_scale_of(float amax)
+{
+    float scale = amax / 448.0f;
+    if (scale != scale) scale = __uint_as_float(kQuietNan);
+    if (scale == 0.0f) scale = 1.0f;
+    return scale;
+}
 __device__ __forceinline__ uint32_t e4m3_code(float v)
 {
     const uint32_t u = __float_as_uint(v);
@@ -443,8 +461,9 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
 // does for every finite input below 464 in magnitude (subnormals and zeros
 // included); it was compared with e4m3_code on all 2^32 fp32 patterns.  At and
 // above 464, for infinities and for NaN it returns a NaN code instead, so those
-// quotients take e4m3_code (saturation to 448, NaN with its sign).  A block's
-// quotients stay at or below 448 unless its maximum is infinite or NaN.
+// quotients take e4m3_code (saturation to 448), and a NaN quotient the NaN code
+// with the sign bit of its value.  A block's quotients stay at or below 448
+// unless its maximum is infinite or NaN.
 __device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
 {
     float q[kGroup];
@@ -457,32 +476,30 @@ __device__ __forceinline__ uint32_t pack_e4m3(const F4& x, float scale)
     for (int k = 0; k < kGroup; ++k) special |= (__float_as_uint(q[k]) & 0x7FFFFFFFu) >= 0x43E80000u;
     if (special) {
 #pragma unroll
-        for (int k = 0; k < kGroup; ++k)
-            if ((__float_as_uint(q[k]) & 0x7FFFFFFFu) >= 0x43E80000u)
-                packed = (packed & ~(0xFFu << (8 * k))) | (e4m3_code(q[k]) << (8 * k));
+        for (int k = 0; k < kGroup; ++k) {
+            const uint32_t a = __float_as_uint(q[k]) & 0x7FFFFFFFu;
+            if (a >= 0x43E80000u) {
+                const uint32_t code = a > 0x7F800000u
+                                          ? ((__float_as_uint(x.v[k]) >> 24) & 0x80u) | 0x7Fu
+                                          : e4m3_code(q[k]);
+                packed = (packed & ~(0xFFu << (8 * k))) | (code << (8 * k));
+            }
+        }
     }
     return packed;
 }
 
 // Scale of the 16-value block held by lanes 4q..4q+3 (4 consecutive values
 // each): the lanes' maxima combined with two butterfly shuffles.  Every lane
-// of the wave must call it.  A NaN never wins a comparison.
+// of the wave must call it.
 __device__ __forceinline__ float block16_scale(const F4& x)
 {
     float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-        const float a = __builtin_fabsf(x.v[k]);
-        amax = a > amax ? a : amax;
-    }
+    for (int k = 0; k < kGroup; ++k) amax = nan_max(amax, __builtin_fabsf(x.v[k]));
 #pragma unroll
-    for (int off = 1; off < 4; off <<= 1) {
-        const float o = __shfl_xor(amax, off, kWave);
-        amax = o > amax ? o : amax;
-    }
-    float scale = amax / 448.0f;
-    if (scale == 0.0f) scale = 1.0f;
-    return scale;
+    for (int off = 1; off < 4; off <<= 1) amax = nan_max(amax, __shfl_xor(amax, off, kWave));
+    return block_scale_of(amax);
 }
 
 __device__ __forceinline__ void store_codes4(uint8_t* p, uint32_t packed)
@@ -754,13 +771,9 @@ __global__ __launch_bounds__(kBlock) void k_fp8_blocks(const float* __restrict__
         for (int i = 0; i < block; i += kGroup) {
             const F4 v = load_f4<true>(x + i, kGroup);
 #pragma unroll
-            for (int k = 0; k < kGroup; ++k) {
-                const float a = __builtin_fabsf(v.v[k]);
-                amax = a > amax ? a : amax;
-            }
+            for (int k = 0; k < kGroup; ++k) amax = nan_max(amax, __builtin_fabsf(v.v[k]));
         }
-        float scale = amax / 448.0f;
-        if (scale == 0.0f) scale = 1.0f;
+        const float scale = block_scale_of(amax);
         for (int i = 0; i < block; i += 16) {
             u32x4 w;
             w.x = pack_e4m3(load_f4<true>(x + i, kGroup), scale);

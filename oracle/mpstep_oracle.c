@@ -47,6 +47,10 @@
  *  - FP8: the chapter's E4M3 emulator is not printed; or_e4m3 rounds to
  *    nearest, ties to even, saturates at the largest finite value 448 (E4M3
  *    has no infinity), and maps NaN to S.1111.111.
+ *  - FP8 blocks holding a NaN: the listing's maximum propagates NaN, so the
+ *    block's scale is NaN (the quiet NaN 0x7FC00000) and each of its codes is
+ *    the NaN code with the sign bit of its value; a NaN quotient of inf / inf
+ *    takes the value's sign too.
  */
 #include <math.h>
 #include <stdint.h>
@@ -487,8 +491,23 @@ float or_e4m3_value(uint8_t c)
     return (float)(s ? -v : v);
 }
 
+/* x / scale for the cast.  The quotient is NaN when the block's scale is NaN
+ * or for inf / inf; IEEE 754 leaves the sign of a NaN result open, and this
+ * reading gives it the sign of x (the sign rule of division, scales being
+ * positive), so that the code does not depend on a machine's default NaN. */
+static float or_fp8_quotient(float x, float scale)
+{
+    float q = x / scale;
+    if (isnan(q)) q = copysignf(NAN, x);
+    return q;
+}
+
 /* Returns 0, or -1 when n is not a multiple of block (the listing refuses a
- * last dimension that the block size does not divide). */
+ * last dimension that the block size does not divide).
+ * The block maximum is the listing's np.max of |x|: a NaN anywhere in the block
+ * makes it NaN, so the block's scale is NaN (written as the quiet NaN
+ * 0x7FC00000, NumPy fixing no payload) and every quotient, hence every code of
+ * the block, is NaN. */
 int or_fp8_block_cast(const float* x, int64_t n, int32_t block, uint8_t* codes, float* scales)
 {
     if (block <= 0 || n % block != 0) return -1;
@@ -497,12 +516,17 @@ int or_fp8_block_cast(const float* x, int64_t n, int32_t block, uint8_t* codes, 
         float amax = 0.0f;
         for (int32_t i = 0; i < block; ++i) {
             float a = fabsf(xb[i]);
-            if (a > amax) amax = a;
+            if (isnan(a) || a > amax) amax = a;
         }
         float scale = amax / 448.0f;
+        if (isnan(scale)) {
+            const uint32_t quiet_nan = 0x7FC00000u;
+            memcpy(&scale, &quiet_nan, sizeof scale);
+        }
         if (scale == 0.0f) scale = 1.0f;
         scales[b] = scale;
-        for (int32_t i = 0; i < block; ++i) codes[b * block + i] = or_e4m3(xb[i] / scale);
+        for (int32_t i = 0; i < block; ++i)
+            codes[b * block + i] = or_e4m3(or_fp8_quotient(xb[i], scale));
     }
     return 0;
 }

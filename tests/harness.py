@@ -220,6 +220,61 @@ class DeviceRun:
         self.model.close()
 
 
+def bits(a):
+    """The bit patterns of a float32 or 16-bit array (so NaNs and signed zeros compare exactly)."""
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)
+
+
+def compare_state(got, want, prev_master, prev_m, w, same_norm, dt, where=""):
+    """Compare one tensor's (or one window's) device state with the oracle's.
+
+    got, want: dicts of "master", "m", "v" (float32) and "w16" (uint16 bit patterns).
+    prev_master, prev_m: the oracle's values before the step (for the tolerance bounds).
+    same_norm: both sides used the same fp32 norm and clip coefficient, so every value
+    must be the same bits; otherwise the parity bar's tolerances apply.
+    Returns the number of 16-bit weights that differ from the oracle's; raises
+    AssertionError on any violation."""
+    # the 16-bit weight is the RNE cast of the device's own master, bit for bit
+    assert np.array_equal(got["w16"], oracle.rd16(got["master"], dt)), "w16 != rd16(master)" + where
+    if same_norm:
+        for nm in ("master", "m", "v", "w16"):
+            a, b = bits(got[nm]), bits(want[nm])
+            bad = a != b
+            if bad.any():
+                idx = int(np.flatnonzero(bad)[0])
+                raise AssertionError("%s bits differ%s: index %d gpu %r oracle %r"
+                                     % (nm, where, idx, got[nm][idx], want[nm][idx]))
+        return 0
+    # non-finite values carry no rounding: same bits, same places
+    for nm in ("master", "m", "v"):
+        a, b = got[nm], want[nm]
+        fin = np.isfinite(b)
+        assert np.array_equal(np.isfinite(a), fin), nm + " non-finite pattern" + where
+        assert np.array_equal(bits(a[~fin]), bits(b[~fin])), nm + " non-finite bits" + where
+    # tolerance of the parity bar: 2e-6 relative to the magnitude of the terms each
+    # value is made of (so cancellation near 0 is judged fairly)
+    rtol = 2e-6
+    b1 = np.float64(np.float32(w.hp["beta1"]))
+    lam = w.hp["lr"] * w.hp["weight_decay"]
+    fin = np.isfinite(want["v"])
+    r_v = want["v"][fin].astype(np.float64)
+    assert rel_within(got["v"][fin], r_v, rtol * np.abs(r_v) + 1e-45).all(), "v tolerance" + where
+    fin = np.isfinite(want["m"])
+    r_m, m0 = want["m"][fin].astype(np.float64), prev_m[fin].astype(np.float64)
+    bound_m = rtol * (b1 * np.abs(m0) + np.abs(r_m - b1 * m0)) + 1e-45
+    assert rel_within(got["m"][fin], r_m, bound_m).all(), "m tolerance" + where
+    fin = np.isfinite(want["master"])
+    r_w, w0 = want["master"][fin].astype(np.float64), prev_master[fin].astype(np.float64)
+    bound_w = rtol * (np.abs(w0) * (1 + lam) + np.abs(w0 - r_w)) + 1e-45
+    assert rel_within(got["master"][fin], r_w, bound_w).all(), "master tolerance" + where
+    # a 16-bit weight may differ only where the two masters differ
+    diff16 = bits(got["w16"]) != bits(want["w16"])
+    diff32 = bits(got["master"]) != bits(want["master"])
+    assert not (diff16 & ~diff32).any(), "w16 differs where the masters agree" + where
+    return int(diff16.sum())
+
+
 def rel_within(x, r, bound):
     """|x - r| <= bound elementwise (all arrays float64)."""
     return np.abs(x.astype(np.float64) - r.astype(np.float64)) <= bound
@@ -261,31 +316,10 @@ def compare_step(dev, orc, w, step, acc_dev=None, acc_orc=None):
     dt = oracle_dtype(w)
     mism = 0
     for t in range(len(masters)):
-        # the 16-bit weight is the RNE cast of the device's own master, bit for bit
-        assert np.array_equal(w16[t], oracle.rd16(masters[t], dt)), "w16 != rd16(master)"
-        if same_norm:
-            for a, b, nm in ((masters[t], o.masters[t], "master"), (m[t], o.m[t], "m"),
-                             (v[t], o.v[t], "v"), (w16[t], o.w16[t], "w16")):
-                bad = a.view(a.dtype) != b
-                if bad.any():
-                    idx = int(np.flatnonzero(bad)[0])
-                    raise AssertionError("%s bits differ: tensor %d index %d gpu %r oracle %r"
-                                         % (nm, t, idx, a[idx], b[idx]))
-        else:
-            # tolerance of the parity bar: 2e-6 relative to the magnitude of the
-            # terms each value is made of (so cancellation near 0 is judged fairly)
-            rtol = 2e-6
-            b1 = np.float64(np.float32(w.hp["beta1"]))
-            lam = w.hp["lr"] * w.hp["weight_decay"]
-            r_v = o.v[t].astype(np.float64)
-            assert rel_within(v[t], r_v, rtol * np.abs(r_v) + 1e-45).all(), "v tolerance"
-            r_m, m0 = o.m[t].astype(np.float64), orc.prev_m[t].astype(np.float64)
-            bound_m = rtol * (b1 * np.abs(m0) + np.abs(r_m - b1 * m0)) + 1e-45
-            assert rel_within(m[t], r_m, bound_m).all(), "m tolerance"
-            r_w, w0 = o.masters[t].astype(np.float64), orc.prev_master[t].astype(np.float64)
-            bound_w = rtol * (np.abs(w0) * (1 + lam) + np.abs(w0 - r_w)) + 1e-45
-            assert rel_within(masters[t], r_w, bound_w).all(), "master tolerance"
-            mism += int((w16[t] != o.w16[t]).sum())
+        got = {"master": masters[t], "m": m[t], "v": v[t], "w16": w16[t]}
+        want = {"master": o.masters[t], "m": o.m[t], "v": o.v[t], "w16": o.w16[t]}
+        mism += compare_state(got, want, orc.prev_master[t], orc.prev_m[t], w, same_norm, dt,
+                              " (tensor %d)" % t)
     rep["w16_mismatch"] = mism
     return rep
 
@@ -413,30 +447,12 @@ def compare_windows(dev, so, w):
         got = {"master": dev.model.master[t][sl].cpu().numpy(),
                "m": dev.model.m[t][sl].cpu().numpy(), "v": dev.model.v[t][sl].cpu().numpy(),
                "w16": dev.model.w16[t][sl].cpu().view(torch.int16).numpy().view(np.uint16)}
-        assert np.array_equal(got["w16"], oracle.rd16(got["master"], so.dt)), "w16 != rd16(master)"
-        for name in ("master", "m", "v", "w16"):
-            a, b = got[name], ost[name]
-            if same:
-                if not np.array_equal(a, b):
-                    idx = int(np.flatnonzero(a != b)[0])
-                    raise AssertionError("%s differs: tensor %d element %d gpu %r oracle %r"
-                                         % (name, t, start + idx, a[idx], b[idx]))
-            elif name == "w16":
-                mism += int((a != b).sum())
-            else:
-                # 2e-6 relative to the magnitude of the terms each value is made of
-                b64 = b.astype(np.float64)
-                if name == "v":
-                    bound = 2e-6 * np.abs(b64)
-                elif name == "m":
-                    b1 = np.float64(np.float32(w.hp["beta1"]))
-                    m0 = ost["prev_m"].astype(np.float64)
-                    bound = 2e-6 * (b1 * np.abs(m0) + np.abs(b64 - b1 * m0))
-                else:
-                    w0 = ost["prev_master"].astype(np.float64)
-                    lam = w.hp["lr"] * w.hp["weight_decay"]
-                    bound = 2e-6 * (np.abs(w0) * (1 + lam) + np.abs(w0 - b64))
-                assert (np.abs(a.astype(np.float64) - b64) <= bound + 1e-45).all(), name
+        if same:
+            prev_master = prev_m = None
+        else:
+            prev_master, prev_m = ost["prev_master"], ost["prev_m"]
+        mism += compare_state(got, ost, prev_master, prev_m, w, same, so.dt,
+                              " (tensor %d, window at %d)" % (t, start))
     rep["w16_mismatch"] = mism
     rep["windows"] = len(so.windows)
     return rep

@@ -71,7 +71,8 @@ def test_e4m3_every_fp32_value_up_to_448(mp):
 @pytest.mark.parametrize("block", [16, 32, 128, 1024])
 def test_fp8_blocks_match_the_oracle(mp, block):
     """Seeded values whose magnitude varies by block (2^-40 .. 2^40), zero blocks, and blocks
-    holding inf or NaN: codes and scales are bit-exact."""
+    holding inf or NaN (Listing 41.5's maximum propagates NaN: a NaN scale and NaN codes with
+    each value's sign): codes and scales are bit-exact."""
     import torch
     nblocks = 4099
     n = nblocks * block
@@ -84,9 +85,13 @@ def test_fp8_blocks_match_the_oracle(mp, block):
     x[11, 1] = np.nan
     x[13, :] = np.nan
     x[17, 2] = -np.inf
+    x[19, block - 1] = np.uint32(0xFFC00000).view(np.float32)     # a NaN with the sign bit set
+    x[23, 0] = np.inf                                             # NaN and inf: NaN wins
+    x[23, 1] = np.nan
     x = x.ravel()
     codes, scales = _cast(mp, torch.from_numpy(x).cuda(), block)
     want_c, want_s = oracle.fp8_block_cast(x, block)
+    assert np.isnan(want_s[[11, 13, 19, 23]]).all() and want_s[7] == np.inf
     assert np.array_equal(scales.view(np.uint32), want_s.view(np.uint32))
     assert np.array_equal(codes, want_c)
 
@@ -102,21 +107,32 @@ def test_fp8_argument_errors(mp):
         assert e.value.status == mp.MP_ERR_INVALID
 
 
-@pytest.mark.parametrize("name", ["edges", "edges-fp16-b16", "llama3-8B-small"])
-def test_adamw_fp8_fused_matches_the_oracle(mp, name):
+@pytest.mark.parametrize("name,nan_master", [("edges", False), ("edges-fp16-b16", False),
+                                              ("llama3-8B-small", False), ("edges", True)])
+def test_adamw_fp8_fused_matches_the_oracle(mp, name, nan_master):
     """mp_adamw_step_fp8: the step equals the oracle exactly as mp_adamw_step does, and every cast
     tensor's codes and scales equal the oracle's block-16 cast of the new masters, bit for bit.
     Tensors whose numel is not a multiple of 16 are left uncast; on a skipped step (the fp16 list
-    injects an inf) nothing is written."""
+    injects an inf) nothing is written.  With nan_master, one master of two cast tensors starts
+    as a NaN (on both sides): the gradients stay finite, so the steps are taken, the NaN stays
+    and its 16-value block casts with a NaN scale and NaN codes (Listing 41.5's maximum)."""
     import torch
     from inputs import configs
     from harness import OracleRun, DeviceRun, compare_step
     w = configs.make(name)
-    say("workload %s: %d tensors, k=%d, %d steps" % (name, len(w.tensors), w.k, w.steps))
+    say("workload %s: %d tensors, k=%d, %d steps, NaN master %s"
+        % (name, len(w.tensors), w.k, w.steps, nan_master))
     orc = OracleRun(w)
     dev = DeviceRun(w)
     cast = [t for t, n in enumerate(w.numels) if n % 16 == 0]
     assert cast
+    if nan_master:
+        quiet = np.uint32(0x7FC00000).view(np.float32)
+        for t in (w.numels.index(256), w.numels.index(65537 - 1)):
+            i = w.numels[t] // 2 + 3
+            orc.st.masters[t][i] = quiet
+            dev.model.master[t][i] = float("nan")
+            assert dev.model.master[t][i:i + 1].cpu().numpy().view(np.uint32)[0] == 0x7FC00000
     codes = [None] * len(w.numels)
     scales = [None] * len(w.numels)
     for t in cast:
@@ -137,6 +153,8 @@ def test_adamw_fp8_fused_matches_the_oracle(mp, name):
                     want = prev[t]
                 else:
                     want = oracle.fp8_block_cast(masters[t], 16)
+                    if nan_master and np.isnan(masters[t]).any():
+                        assert np.isnan(want[1]).sum() == 1
                     # the device masters are the oracle's whenever the norms agree bit for bit
                     if rep["same_norm_bits"]:
                         assert np.array_equal(masters[t].view(np.uint32),

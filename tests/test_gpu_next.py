@@ -179,10 +179,11 @@ def test_flattened_buffers(mp, name):
 
 def test_whole_model_as_one_tensor(mp):
     """A caller who flattens the whole model into one buffer per kind passes a one-tensor plan
-    (the chunk table then cuts one range): the update equals the per-tensor oracle."""
+    (the chunk table then cuts one range): masters, moments and 16-bit weights equal the
+    per-tensor oracle's, bit for bit when the norms agree, else within the parity bar."""
     import torch
     import inputs
-    from harness import OracleRun
+    from harness import OracleRun, compare_state, oracle_dtype
     w = configs.make("llama3-8B-small")
     orc = OracleRun(w)
     total = w.total
@@ -211,15 +212,21 @@ def test_whole_model_as_one_tensor(mp):
             mp.mp_adamw_step(plan, st, sets[-1], wts[-1], 0, hp)
             mp.mp_scaler_update(st)
             stats = mp.read_stats(st)
+            assert stats["found_inf"] == 0 and stats["step"] == orc.st.clock.t
             assert abs(stats["grad_norm"] - orc.st.norm) <= 1e-5 * orc.st.norm
-            same = np.float32(stats["grad_norm"]) == np.float32(orc.st.norm)
-            master = bufs["master"].cpu().numpy()
+            same = (np.float32(stats["grad_norm"]) == np.float32(orc.st.norm)
+                    and np.float32(stats["clip_coef"]) == np.float32(orc.st.coef))
+            host = {name: bufs[name].cpu().numpy() for name in ("master", "m", "v")}
+            host["w16"] = w16.cpu().view(torch.int16).numpy().view(np.uint16)
+            mism = 0
             for t, (o, n) in enumerate(zip(offs, w.numels)):
-                if same:
-                    assert np.array_equal(master[o:o + n], orc.st.masters[t])
-                else:
-                    assert np.allclose(master[o:o + n], orc.st.masters[t], rtol=2e-6, atol=1e-9)
-            say("  step", s, "norm", stats["grad_norm"], "same bits", bool(same))
+                got = {name: a[o:o + n] for name, a in host.items()}
+                want = {"master": orc.st.masters[t], "m": orc.st.m[t], "v": orc.st.v[t],
+                        "w16": orc.st.w16[t]}
+                mism += compare_state(got, want, orc.prev_master[t], orc.prev_m[t], w, same,
+                                      oracle_dtype(w), " (tensor %d)" % t)
+            say("  step", s, "norm", stats["grad_norm"], "same bits", bool(same),
+                "w16 mismatches", mism)
     finally:
         for g in sets:
             mp.mp_gradset_destroy(g)

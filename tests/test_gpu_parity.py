@@ -347,6 +347,17 @@ def test_call_order_and_argument_errors(mp):
         with pytest.raises(mp.MpError) as e:
             mp.mp_adamw_step(plan, st, g, 0.5, 0, dev.hp)
         assert e.value.status == mp.MP_ERR_ORDER
+        # so does pointing the folded micro-batch's gradset at (other, or even the same)
+        # buffers: the norm measured what the old pointers held
+        mp.mp_scaler_update(st)
+        mp.mp_unscale_check_norm(plan, st, g, 0.5, 0, 1.0)
+        mp.mp_gradset_update(g, dev.g16[0])
+        with pytest.raises(mp.MpError) as e:
+            mp.mp_adamw_step(plan, st, g, 0.5, 0, dev.hp)
+        assert e.value.status == mp.MP_ERR_ORDER
+        with pytest.raises(mp.MpError) as e:          # the group form takes the same check
+            mp.mp_adamw_step_group(plan, st, [g], [0.5], 0, dev.hp)
+        assert e.value.status == mp.MP_ERR_ORDER
         # one scaler decision per measured step
         mp.mp_scaler_update(st)
         with pytest.raises(mp.MpError) as e:

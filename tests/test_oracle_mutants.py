@@ -98,9 +98,10 @@ MUTANTS = [
      "return params * (2 + 4 + 4 + 4);"),
     ("fp8-scale-without-abs", C, "float a = fabsf(xb[i]);", "float a = xb[i];"),
     ("fp8-zero-block-scale", C, "if (scale == 0.0f) scale = 1.0f;", ""),
-    ("fp8-multiplies-by-scale", C, "codes[b * block + i] = or_e4m3(xb[i] / scale);",
-     "codes[b * block + i] = or_e4m3(xb[i] * scale);"),
+    ("fp8-multiplies-by-scale", C, "float q = x / scale;", "float q = x * scale;"),
     ("fp8-scale-wrong-max", C, "float scale = amax / 448.0f;", "float scale = amax / 480.0f;"),
+    ("fp8-max-ignores-nan", C, "if (isnan(a) || a > amax) amax = a;", "if (a > amax) amax = a;"),
+    ("fp8-nan-quotient-sign-from-machine", C, "if (isnan(q)) q = copysignf(NAN, x);", ""),
     ("e4m3-truncates", C, "Y = nearbyint(X / quantum) * quantum;", "Y = trunc(X / quantum) * quantum;"),
     ("e4m3-bias", C, "return (uint8_t)(sign | (uint32_t)((e + 7) << 3) | mant);",
      "return (uint8_t)(sign | (uint32_t)((e + 8) << 3) | mant);"),

@@ -734,6 +734,38 @@ def test_fp8_block_cast_follows_the_listing():
         oracle.fp8_block_cast(np.zeros(17, np.float32), 16)
 
 
+def test_fp8_block_with_nan_follows_the_listing():
+    """Listing 41.5 takes the block scale with np.max, which propagates NaN: a block holding one
+    NaN gets a NaN scale (written as the quiet NaN 0x7FC00000) and every value of it a NaN code,
+    whose sign bit is the value's; a block whose maximum is infinite gets an infinite scale, its
+    finite values code to signed zero and inf / inf to NaN with the value's sign."""
+    x = np.linspace(-3.0, 3.0, 64).astype(np.float32)
+    x[16 + 5] = np.nan                       # block 1: one NaN among finite values of both signs
+    x[32 + 2] = np.inf                       # block 2: +inf and -inf, the rest finite
+    x[32 + 9] = -np.inf
+    x[48:64] = 0.0
+    x[48 + 7] = np.nan                       # block 3: NaN among zeros
+    codes, scales = oracle.fp8_block_cast(x, 16)
+    blocks = x.reshape(-1, 16)
+    with np.errstate(invalid="ignore"):
+        listing = np.max(np.abs(blocks), axis=-1) / np.float32(448.0)
+    listing = np.where(listing == 0, np.float32(1.0), listing).astype(np.float32)
+    assert np.array_equal(np.isnan(scales), np.isnan(listing))
+    assert np.isnan(scales[[1, 3]]).all()
+    assert (scales.view(np.uint32)[[1, 3]] == 0x7FC00000).all()
+    fin = ~np.isnan(listing)
+    assert np.array_equal(scales[fin], listing[fin])
+    assert scales[2] == np.inf
+    sign = (x.view(np.uint32) >> 24).astype(np.uint8) & 0x80
+    for b in (1, 3):
+        c = codes[16 * b:16 * b + 16]
+        assert np.array_equal(c, sign[16 * b:16 * b + 16] | 0x7F)
+    c2 = codes[32:48]
+    assert c2[2] == 0x7F and c2[9] == 0xFF
+    rest = np.array([i for i in range(16) if i not in (2, 9)])
+    assert np.array_equal(c2[rest], sign[32 + rest])      # finite / inf = signed zero
+
+
 def test_fp8_block_scales_help_the_small_block():
     """Section 41.5: one scale for a whole tensor forces small blocks onto a coarse step; a scale
     per block keeps their relative precision."""
