@@ -342,6 +342,27 @@ mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last,
                          int32_t last_is_first, float max_norm, const mp_adamw_hparams* hp,
                          mp_stream stream);
 
+/* mp_update_step for callers that cannot allocate device memory while they
+ * run: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, checks, order rules and results as
+ * mp_update_step, but the norm pass keeps its partial sums in a static device
+ * array of the library (MP_NOALLOC_MAX_NORM_BLOCKS + 256 doubles, about 2 MB,
+ * one copy per device held until the process ends) instead of the plan's own
+ * buffer, and the call allocates nothing.  The norm's first stage takes one
+ * partial per block; a plan whose norm pass takes more than
+ * MP_NOALLOC_MAX_NORM_BLOCKS blocks is refused with MP_ERR_INVALID before
+ * anything is enqueued (one block per chunk of 2048 elements, or per 16 chunks
+ * when the pass reads the last micro-batch alone: plans of up to about 537M
+ * parameters, or 8.6G with last_is_first).  Each launch writes every partial it
+ * later reads, so nothing needs clearing between calls.  All calls on one
+ * device share that one array: calls that may overlap on a device (two streams,
+ * two threads) race and must be serialised by the caller.  The plan's device
+ * address of the array is looked up when the plan is created. */
+#define MP_NOALLOC_MAX_NORM_BLOCKS 262144
+mp_status mp_update_step_noalloc(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                                 float w_last, int32_t last_is_first, float max_norm,
+                                 const mp_adamw_hparams* hp, mp_stream stream);
+
 /* mp_update_step with the last n micro-batches (1 <= n <= 4) resident and all
  * folded into the norm pass and the AdamW pass, as `last` is folded in for
  * n = 1.  The gradient of each element is the accumulator (skipped when

@@ -33,10 +33,11 @@ ENTRY_POINTS = [
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
     "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_group",
     "mp_update_step_group", "mp_unscale_check_norm_group", "mp_adamw_step_group",
-    "mp_norm_partial_group",
+    "mp_norm_partial_group", "mp_update_step_noalloc",
 ]
 
 MP_STATE_BLOB_BYTES = 256
+MP_NOALLOC_MAX_NORM_BLOCKS = 262144
 
 
 class MpError(RuntimeError):
@@ -120,6 +121,8 @@ def _bind(L):
         "mp_adamw_step_fp8": ([P, P, P, f32, i32, ctypes.POINTER(AdamWHparams), P, P], i32),
         "mp_gradset_update": ([P, PP, P], i32),
         "mp_update_step": ([P, P, P, f32, i32, f32, ctypes.POINTER(AdamWHparams), P], i32),
+        "mp_update_step_noalloc": ([P, P, P, f32, i32, f32, ctypes.POINTER(AdamWHparams), P],
+                                   i32),
         "mp_token_weights_dev": ([i32, P, P, P], i32),
         "mp_accumulate_group": ([P, PP, P, i32, i32, i32, P], i32),
         "mp_update_step_group": ([P, P, PP, P, i32, i32, i32, f32, ctypes.POINTER(AdamWHparams),
@@ -314,6 +317,13 @@ def mp_adamw_step(plan, state, last, w_last, last_is_first, hp, stream=None):
 def mp_update_step(plan, state, last, w_last, last_is_first, max_norm, hp, stream=None):
     _check(lib().mp_update_step(plan, state, last, float(w_last), int(bool(last_is_first)),
                                 float(max_norm), ctypes.byref(hp), _stream(stream)))
+
+
+def mp_update_step_noalloc(plan, state, last, w_last, last_is_first, max_norm, hp, stream=None):
+    """mp_update_step with the norm's scratch in the library's static device array."""
+    _check(lib().mp_update_step_noalloc(plan, state, last, float(w_last),
+                                        int(bool(last_is_first)), float(max_norm),
+                                        ctypes.byref(hp), _stream(stream)))
 
 
 def mp_unscale_check_norm_group(plan, state, sets, weights, last_is_first, max_norm,

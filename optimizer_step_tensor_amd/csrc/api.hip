@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -78,9 +79,43 @@ struct mp_state {
     bool decision_pending;
 };
 
+// Norm scratch of mp_update_step_noalloc, for callers that cannot allocate:
+// first-stage partial sums, then the second-stage sums.  Each device holds its
+// own copy for the life of the process; host code uses the per-device address
+// from hipGetSymbolAddress, never this name.
+static __device__ __align__(256) double scratch[MP_NOALLOC_MAX_NORM_BLOCKS + mpk::kNormStage2];
+
 namespace {
 
 thread_local std::string g_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+double* g_scratch[kMaxDevices];              // device address of `scratch`, per device
+hipError_t g_scratch_error[kMaxDevices];     // the lookup's result, once made
+
+// Look up this device's copy of `scratch` once (the device must be current).
+// Called when a plan is created, so that the hot call itself never loads code
+// or touches the runtime's module tables.
+void setup_scratch(int device)
+{
+    if (device < 0 || device >= kMaxDevices) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[device] != nullptr) return;
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_error[device] = e;
+    if (e == hipSuccess) g_scratch[device] = static_cast<double*>(ptr);
+}
+
+double* scratch_of(int device, hipError_t* err)
+{
+    *err = hipErrorInvalidDevice;
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    *err = g_scratch[device] != nullptr ? hipSuccess : g_scratch_error[device];
+    return g_scratch[device];
+}
 
 mp_status fail(mp_status st, const char* fmt, ...)
 {
@@ -422,6 +457,7 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
         int device = 0;
         hipError_t e = hipGetDevice(&device);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        setup_scratch(device);
         const int cus = device_cus(device);
         const int64_t grid_cap = MPK_ELEM_BLOCKS_PER_CU > 0 ? int64_t(cus) * MPK_ELEM_BLOCKS_PER_CU
                                                              : int64_t(1) << 30;
@@ -786,8 +822,9 @@ mp_status accumulate(mp_plan* plan, const Group& g, int32_t first, mp_stream str
     return ok();
 }
 
+// partials: norm_blocks + kNormStage2 doubles of device scratch (NULL: the plan's)
 mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, float max_norm,
-                             mp_stream stream)
+                             mp_stream stream, double* partials = nullptr)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     mp_status st = check_group(plan, g);
@@ -796,8 +833,8 @@ mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, flo
     st = check_devices(plan, state);
     if (st != MP_OK) return st;
     hipError_t e = mpk::launch_norm(view(plan), plan->norm_grid, device_group(g), plan->dtype,
-                                    plan->d_partials, max_norm, state->d,
-                                    static_cast<hipStream_t>(stream));
+                                    partials != nullptr ? partials : plan->d_partials, max_norm,
+                                    state->d, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm launch");
     state->decision_pending = true;
     plan->partial_pending = false;
@@ -831,7 +868,7 @@ mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_ad
 }
 
 mp_status update_step(mp_plan* plan, mp_state* state, const Group& g, float max_norm,
-                      const mp_adamw_hparams* hp, mp_stream stream)
+                      const mp_adamw_hparams* hp, mp_stream stream, bool noalloc = false)
 {
     // every structural check first, so that an error enqueues nothing
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
@@ -841,7 +878,18 @@ mp_status update_step(mp_plan* plan, mp_state* state, const Group& g, float max_
         st = fail(MP_ERR_INVALID, "max_norm must be finite");
     if (st == MP_OK) st = check_devices(plan, state);
     if (st != MP_OK) return st;
-    st = unscale_check_norm(plan, state, g, max_norm, stream);
+    double* partials = nullptr;
+    if (noalloc) {
+        const int blocks = mpk::norm_blocks(plan->norm_grid, device_group(g));
+        if (blocks > MP_NOALLOC_MAX_NORM_BLOCKS)
+            return fail(MP_ERR_INVALID, "the norm pass of this plan takes %d blocks; "
+                        "mp_update_step_noalloc holds the partial sums of at most %d",
+                        blocks, MP_NOALLOC_MAX_NORM_BLOCKS);
+        hipError_t e = hipSuccess;
+        partials = scratch_of(plan->device, &e);
+        if (partials == nullptr) return hip_fail(e, "scratch of mp_update_step_noalloc");
+    }
+    st = unscale_check_norm(plan, state, g, max_norm, stream, partials);
     if (st == MP_OK) st = adamw_step(plan, state, g, hp, nullptr, stream, true);
     return st;
 }
@@ -971,6 +1019,14 @@ mp_status mp_update_step(mp_plan* plan, mp_state* state, const mp_gradset* last,
 {
     return update_step(plan, state, single(last, host_weight(w_last), last_is_first), max_norm,
                        hp, stream);
+}
+
+mp_status mp_update_step_noalloc(mp_plan* plan, mp_state* state, const mp_gradset* last,
+                                 float w_last, int32_t last_is_first, float max_norm,
+                                 const mp_adamw_hparams* hp, mp_stream stream)
+{
+    return update_step(plan, state, single(last, host_weight(w_last), last_is_first), max_norm,
+                       hp, stream, true);
 }
 
 mp_status mp_unscale_check_norm_group(mp_plan* plan, mp_state* state,

@@ -130,6 +130,9 @@ struct Fp8Out {
 // accumulate: acc = the group's terms (first: without the accumulator), n >= 1
 hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int first, int dtype,
                              hipStream_t s);
+// First-stage blocks (= partial sums) of the norm pass over group g on a plan of
+// `grid` blocks; the pass needs that many doubles plus kNormStage2 of scratch.
+int norm_blocks(int grid, const Grads& g);
 hipError_t launch_norm(const PlanView& p, int grid, const Grads& g, int dtype, double* partials,
                        float max_norm, DevState* st, hipStream_t s);
 hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int dtype,

@@ -833,8 +833,7 @@ hipError_t with_group(int dtype, const Grads& g, Fn&& fn)
 hipError_t launch_norm_blocks(const PlanView& p, int grid, const Grads& g, int dtype,
                               double* partials, const DevState* st, hipStream_t s, int* used)
 {
-    int blocks = grid;
-    if (!g.acc && g.n == 1) blocks = grid / kNormChunks16 > 0 ? grid / kNormChunks16 : 1;
+    const int blocks = norm_blocks(grid, g);
     *used = blocks;
     return with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
         k_norm_partial<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value>
@@ -843,6 +842,12 @@ hipError_t launch_norm_blocks(const PlanView& p, int grid, const Grads& g, int d
 }
 
 }  // namespace
+
+int norm_blocks(int grid, const Grads& g)
+{
+    if (!g.acc && g.n == 1) return grid / kNormChunks16 > 0 ? grid / kNormChunks16 : 1;
+    return grid;
+}
 
 hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int first, int dtype,
                              hipStream_t s)

@@ -95,6 +95,7 @@ class DeviceRun:
         self.step_no = 0
         self.fp8set = None                 # set: steps use the fused AdamW + FP8 entry point
         self.one_call = False              # True: steps use mp_update_step
+        self.noalloc = False               # with one_call: mp_update_step_noalloc instead
         self.fold_last = True              # False: accumulate every micro-batch, then norm/AdamW
         self.device_weights = False        # True: weights from device counts, steps use the
         self.dev_counts = None             # group entry points (kept alive until the next step)
@@ -143,8 +144,8 @@ class DeviceRun:
                         if snapshot and self.model.acc is not None else None)
         last, lif = self.gsets[w.k - 1], w.k == 1
         if self.one_call:
-            mp.mp_update_step(self.model.plan, self.state, last, weights[-1], lif, w.max_norm,
-                              self.hp)
+            call = mp.mp_update_step_noalloc if self.noalloc else mp.mp_update_step
+            call(self.model.plan, self.state, last, weights[-1], lif, w.max_norm, self.hp)
             return acc_snapshot
         mp.mp_unscale_check_norm(self.model.plan, self.state, last, weights[-1], lif, w.max_norm)
         if self.fp8set is None:

@@ -40,6 +40,13 @@ def test_every_declared_function_is_exported(mp):
     assert sorted(mp.ENTRY_POINTS) == names
 
 
+def test_header_constants_match_the_binding(mp):
+    src = open(HEADER).read()
+    for name in ("MP_STATE_BLOB_BYTES", "MP_NOALLOC_MAX_NORM_BLOCKS"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
+        assert m and int(m.group(1)) == getattr(mp, name), name
+
+
 def test_status_strings_and_version(mp):
     assert mp.mp_abi_version() == 1
     assert [mp.mp_status_string(s) for s in range(6)] == [
