@@ -207,10 +207,96 @@ def time_save_restore(mp, torch, state, stream, reps=20):
 
 
 EXTRAS = ("device_copy", "fp8_block_cast", "adamw_fp8_fused", "state_save_restore",
-          "zero8_rank_share", "resident_groups")
+          "zero8_rank_share", "resident_groups", "ceiling")
 
 
-def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=None):
+def flat_extent(model, arrays):
+    """(base address, element count) of each flat buffer behind a flat-layout model's views."""
+    from optimizer_step_tensor_amd import _align_elems
+    n = sum(_align_elems(x) for x in model.numels)
+    return [(a[0].data_ptr(), n) for a in arrays], n
+
+
+def time_ceiling(torch, w, model, g16_last, stream, kernel_ms, reps=3):
+    """Bandwidth probes (optimizer_step_tensor_amd/csrc/ceiling.hip) over the model's own flat
+    buffers, in the library's launch shape: the AdamW pass's exact traffic (5 streams read,
+    4 written, trivial arithmetic, state left as it was) at several caps on resident blocks
+    per CU, the norm's read traffic, and a copy and a fill of the (dead) accumulator.  The
+    step's AdamW and norm launch times are rated against the fastest probe of their own
+    pattern."""
+    from optimizer_step_tensor_amd import build as lib_build
+    if model.layout != "flat" or model.acc is None:
+        return {"skipped": "needs the flat layout and an accumulator"}
+    C = ctypes.CDLL(lib_build.CEILING_LIB)
+    i64, i32, P_, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    C.mpc_adamw_pattern.argtypes = [P_, P_, P_, P_, P_, P_, i64, i32, i32, i32, P_]
+    C.mpc_read_pattern.argtypes = [P_, P_, i64, P_, i32, i32, P_]
+    C.mpc_copy_pattern.argtypes = [P_, P_, i64, i32, i32, P_]
+    C.mpc_fill_pattern.argtypes = [P_, i64, f32, i32, i32, P_]
+    for f in (C.mpc_adamw_pattern, C.mpc_read_pattern, C.mpc_copy_pattern, C.mpc_fill_pattern):
+        f.restype = i32
+    (acc, master, m, v, w16, g), n = flat_extent(
+        model, [model.acc, model.master, model.m, model.v, model.w16, g16_last])
+    acc, master, m, v, w16, g = [x[0] for x in (acc, master, m, v, w16, g)]
+    sink = torch.empty((n + 2047) // 2048, dtype=torch.float32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fp16 = int(model.dtype != 0)
+
+    def timed(fn):
+        assert fn() == 0
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            assert fn() == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"elements": n, "reps": reps, "shape": "one 256-lane block per 2048 elements, "
+                                                  "XCD runs of `span` chunks, nontemporal"}
+    adam_bytes, read_bytes = 32 * n, 6 * n
+    pat = {}
+    for cap in (0, 3, 4, 5):
+        for span in (64, 128):
+            ms = timed(lambda: C.mpc_adamw_pattern(acc, g, master, m, v, w16, n, fp16, cap, span,
+                                                   sp))
+            pat["cap%d_span%d" % (cap, span)] = {"ms": ms, "GBps": adam_bytes / ms / 1e6}
+    best = max(pat.values(), key=lambda r: r["GBps"])
+    out["adamw_pattern"] = {"bytes_per_element": 32, "runs": pat, "best_GBps": best["GBps"],
+                            "best_frac": best["GBps"] / HBM_PEAK_GBPS}
+    rd = {}
+    for cap in (0,):
+        for span in (64, 128):
+            ms = timed(lambda: C.mpc_read_pattern(acc, g, n, sink.data_ptr(), cap, span, sp))
+            rd["cap%d_span%d" % (cap, span)] = {"ms": ms, "GBps": read_bytes / ms / 1e6}
+    best_rd = max(rd.values(), key=lambda r: r["GBps"])
+    out["norm_pattern"] = {"bytes_per_element": 6, "runs": rd, "best_GBps": best_rd["GBps"],
+                           "best_frac": best_rd["GBps"] / HBM_PEAK_GBPS}
+    # the accumulator is dead between steps (the next first accumulation overwrites it)
+    for name, fn, bpe in (
+            ("copy_in_place", lambda cap: C.mpc_copy_pattern(acc, acc, n, cap, 128, sp), 8),
+            ("fill", lambda cap: C.mpc_fill_pattern(acc, n, 0.0, cap, 128, sp), 4)):
+        runs = {}
+        for cap in (0, 4):
+            ms = timed(lambda: fn(cap))
+            runs["cap%d" % cap] = {"ms": ms, "GBps": bpe * n / ms / 1e6}
+        b = max(runs.values(), key=lambda r: r["GBps"])
+        out[name] = {"bytes_per_element": bpe, "runs": runs, "best_GBps": b["GBps"],
+                     "best_frac": b["GBps"] / HBM_PEAK_GBPS}
+    P = w.total
+    step_adam = 32 * P / kernel_ms["adamw"] / 1e6
+    step_norm = 6 * P / kernel_ms["norm"] / 1e6
+    out["adamw_vs_pattern"] = step_adam / best["GBps"]
+    out["norm_vs_pattern"] = step_norm / best_rd["GBps"]
+    # the fused step at the speed of its two patterns
+    t_ceil = adam_bytes / best["GBps"] / 1e6 + read_bytes / best_rd["GBps"] / 1e6
+    out["fused_step_pattern_frac"] = (adam_bytes + read_bytes) / t_ceil / 1e6 / HBM_PEAK_GBPS
+    return out
+
+
+def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=None,
+               kernel_ms=None):
     """The rows after the hot path, on the same resident buffers (`only`: a subset of EXTRAS):
     - the runtime's own device-to-device copy of 4 GiB, context for the roofline;
     - the fine-grained FP8 cast (block 16) of every fp32 master;
@@ -220,7 +306,9 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=
     - one rank's share of a ZeRO-8 step: a plan over 1/8 of every tensor (slice boundaries on
       multiples of 64 elements), its accumulate passes, partial norm + finish, AdamW, scaler;
     - the step with all k micro-batch gradients resident, folded in groups of up to four
-      (time_groups).  Same results, bit for bit, as the timed step."""
+      (time_groups).  Same results, bit for bit, as the timed step;
+    - bandwidth probes of the AdamW and norm access patterns at the model's size (time_ceiling),
+      last, since the fill probe overwrites the dead accumulator."""
     def want(name):
         return only is None or name in only
 
@@ -245,6 +333,8 @@ def run_extras(mp, torch, w, model, g16, sets, state, hp, weights, stream, only=
     if want("resident_groups") and w.k >= 2:
         out["resident_groups"] = time_groups(mp, torch, w, model, sets, state, hp, weights,
                                              stream)
+    if want("ceiling") and kernel_ms is not None and w.k >= 2:
+        out["ceiling"] = time_ceiling(torch, w, model, g16[-1], stream, kernel_ms)
     return out
 
 
@@ -566,7 +656,7 @@ def main():
            HBM_PEAK_GBPS * 100, HBM_PEAK_GBPS))
 
     extras = None if args.no_extras else run_extras(mp, torch, w, model, g16, sets, state, hp,
-                                                    weights, stream, only)
+                                                    weights, stream, only, kernel_ms)
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,

@@ -28,6 +28,18 @@ def build(out=LIB, extra=()):
     return out
 
 
+CEILING_SRC = os.path.join(HERE, "csrc", "ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libmpceiling.so")
+
+
+def build_ceiling(out=CEILING_LIB):
+    """The benchmark's bandwidth probes (csrc/ceiling.hip): not part of the library's API."""
+    tmp = out + ".tmp"
+    subprocess.run([HIPCC, *FLAGS, "-o", tmp, CEILING_SRC], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 EXAMPLE_SRC = os.path.join(HERE, "examples", "c_api_step.cpp")
 EXAMPLE = os.path.join(HERE, "examples", "c_api_step")
 
@@ -45,4 +57,5 @@ def build_example():
 
 if __name__ == "__main__":
     print(build())
+    print(build_ceiling())
     print(build_example())

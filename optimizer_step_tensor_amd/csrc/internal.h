@@ -32,6 +32,17 @@ namespace mpk {
 #ifndef MPK_XCD_SPAN
 #define MPK_XCD_SPAN 64            // consecutive chunks per XCD turn; 1: no renumbering
 #endif
+// The passes that write (accumulate, AdamW) take runs of 128 chunks per XCD
+// together with the cap on resident blocks below; the read-only norm keeps 64.
+#ifndef MPK_ACC_XCD_SPAN
+#define MPK_ACC_XCD_SPAN 128
+#endif
+#ifndef MPK_NORM_XCD_SPAN
+#define MPK_NORM_XCD_SPAN MPK_XCD_SPAN
+#endif
+#ifndef MPK_ADAMW_XCD_SPAN
+#define MPK_ADAMW_XCD_SPAN 128
+#endif
 #ifndef MPK_GROUPS_PER_LANE
 #define MPK_GROUPS_PER_LANE 2      // groups of 4 elements per lane per block pass
 #endif
@@ -50,12 +61,42 @@ namespace mpk {
 #ifndef MPK_NT_STORES
 #define MPK_NT_STORES 1            // nontemporal hint on streamed stores
 #endif
+// Resident blocks per CU of each streaming pass (0: as many as registers allow,
+// 7 for AdamW, 8 for the others).  The cap is imposed by reserving a share of
+// the CU's LDS per block.  Timed in alternation on the 8B, 1.3B and ragged
+// lists, 4 blocks per CU (with runs of 128 chunks per XCD) made AdamW 2-4% and
+// the accumulate passes 1-2% faster on all three, while the read-only norm pass
+// only lost from any cap.  Fewer blocks in flight keep fewer DRAM pages open
+// at once; the mix of reads and writes is what suffers from too many.
+#ifndef MPK_ADAMW_BLOCKS_PER_CU
+#define MPK_ADAMW_BLOCKS_PER_CU 4
+#endif
+#ifndef MPK_NORM_BLOCKS_PER_CU
+#define MPK_NORM_BLOCKS_PER_CU 0
+#endif
+#ifndef MPK_ACC_BLOCKS_PER_CU
+#define MPK_ACC_BLOCKS_PER_CU 4
+#endif
+
+constexpr int kLdsPerCu = 160 * 1024;                // LDS of one gfx950 CU
+// Dynamic LDS bytes per block that let at most n blocks share a CU (n = 0: none).
+constexpr unsigned lds_for_blocks_per_cu(int n)
+{
+    return n > 0 ? static_cast<unsigned>(kLdsPerCu / n) & ~1023u : 0u;
+}
 
 constexpr int kBlock = 256;                          // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
 constexpr int kXcds = 8;                             // XCDs per MI355X
 constexpr int kNormStage2 = 256;                     // second-stage sums of the norm
-constexpr int kNormChunks16 = 16;                    // chunks per norm block, one 16-bit stream
+#ifndef MPK_NORM_CHUNKS
+#define MPK_NORM_CHUNKS 1          // consecutive chunks per norm block (several streams)
+#endif
+#ifndef MPK_NORM_CHUNKS16
+#define MPK_NORM_CHUNKS16 16       // consecutive chunks per norm block, one 16-bit stream
+#endif
+constexpr int kNormChunks = MPK_NORM_CHUNKS;
+constexpr int kNormChunks16 = MPK_NORM_CHUNKS16;
 constexpr int kGroup = 4;                            // elements per 16-byte fp32 vector
 constexpr int kGroupsPerLane = MPK_GROUPS_PER_LANE;
 constexpr int kWaveSlab = kWave * kGroup * kGroupsPerLane;   // 512 elements per wave pass

@@ -150,12 +150,13 @@ __device__ __forceinline__ void store_h4(uint16_t* p, const H4& r, int nv)
 }
 
 // The chunk block b of a G-block grid starts at.  Workgroup b runs on XCD
-// b mod 8; this renumbering gives each XCD MPK_XCD_SPAN consecutive chunks per
-// turn of 8 * MPK_XCD_SPAN blocks.  It permutes 0..G-1: blocks of the last,
-// incomplete turn keep their own number.
+// b mod 8; this renumbering gives each XCD SPAN consecutive chunks per turn of
+// 8 * SPAN blocks.  It permutes 0..G-1: blocks of the last, incomplete turn
+// keep their own number.
+template <int SPAN = MPK_XCD_SPAN>
 __device__ __forceinline__ int64_t xcd_first_chunk(int64_t b, int64_t G)
 {
-    constexpr int64_t span = MPK_XCD_SPAN;
+    constexpr int64_t span = SPAN;
     constexpr int64_t turn = span * kXcds;
     if (span <= 1 || b >= (G / turn) * turn) return b;
     const int64_t t = b / turn, within = b % turn;
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p, Grads g)
 {
     float w[kMaxGroup];
     group_weights<NG>(g, w);
-    for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
+    for (int64_t c = xcd_first_chunk<MPK_ACC_XCD_SPAN>(blockIdx.x, gridDim.x); c < p.n_chunks;
          c += gridDim.x) {
         const Chunk ch = p.chunks[c];
         float* acc = p.tensors[ch.tensor].acc + ch.start;
@@ -290,12 +291,37 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p, Grads g)
 }
 
 // ---------------------------------------------------------------------------
-// Unscale + sum of squares, first stage: one binary64 partial per block (one
-// block per chunk by default).  An inf or NaN gradient makes the sum inf or
+// Unscale + sum of squares, first stage: one binary64 partial per block.  Block
+// b takes the CPB consecutive chunks of "super-chunk" b (renumbered for the XCDs
+// like the chunks of the other passes).  When all of them are whole 2048-element
+// chunks, every descriptor is read first and then every data load is issued
+// before the first square is summed, so that the latency of the descriptor
+// reads and of one block's loads is paid once per CPB chunks; a block with a
+// ragged or missing chunk walks its chunks one by one.  The order of the sum is
+// fixed by the grid either way.  An inf or NaN gradient makes the sum inf or
 // NaN; finite fp32 squares cannot overflow binary64 for any element count a
 // device can hold, so the overflow flag is exactly "the sum is not finite".
 // ---------------------------------------------------------------------------
 template <int DT, bool ACC, int NG>
+__device__ __forceinline__ void add_squares(const F4& a, const u32x2 (&h)[kMaxGroup],
+                                            const float (&w)[kMaxGroup], float inv, double& s)
+{
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        uint32_t hk[kMaxGroup];
+#pragma unroll
+        for (int i = 0; i < kMaxGroup; ++i)
+            hk[i] = i < NG ? ((k & 1) ? (h[i][k >> 1] >> 16) : (h[i][k >> 1] & 0xFFFFu)) : 0u;
+        const float gv = grad_sum<DT, ACC, NG>(ACC ? a.v[k] : 0.0f, hk, w) * inv;
+        const double d = static_cast<double>(gv);
+        // the square of an fp32 value is exact in binary64, so this fma is the
+        // same as a rounded add of the exact square; the zeros loaded for
+        // elements past a tail add exactly 0
+        s = __builtin_fma(d, d, s);
+    }
+}
+
+template <int DT, bool ACC, int NG, int CPB>
 __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p, Grads g,
                                                          const DevState* __restrict__ st,
                                                          double* __restrict__ partials)
@@ -304,41 +330,63 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p, Grads g,
     group_weights<NG>(g, w);
     const float inv = st->inv_scale;
     double s = 0.0;
-    for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
-         c += gridDim.x) {
-        const Chunk ch = p.chunks[c];
-        const float* acc = ACC ? p.tensors[ch.tensor].acc + ch.start : nullptr;
-        const uint16_t* gp[kMaxGroup];
+    const int64_t c0 = xcd_first_chunk<MPK_NORM_XCD_SPAN>(blockIdx.x, gridDim.x) * CPB;
+    bool whole = c0 + CPB <= p.n_chunks;
+    Chunk ch[CPB] = {};
 #pragma unroll
-        for (int i = 0; i < NG; ++i) gp[i] = g.set[i][ch.tensor] + ch.start;
-        for_each_pass(ch.len, [&](auto full, int base) {
-            constexpr bool F = decltype(full)::value;
-            int nv[kGroupsPerLane];
-            F4 a[kGroupsPerLane];
-            H4 h[kMaxGroup][kGroupsPerLane];
+    for (int q = 0; q < CPB; ++q) {
+        if (c0 + q < p.n_chunks) ch[q] = p.chunks[c0 + q];
+        whole = whole && ch[q].len == kBlockSlab;
+    }
+    if (whole) {
+        F4 a[CPB][kGroupsPerLane];
+        u32x2 h[CPB][kGroupsPerLane][kMaxGroup];
 #pragma unroll
-            for (int j = 0; j < kGroupsPerLane; ++j) {
-                const int e = base + lane_offset(j);
-                nv[j] = F ? kGroup : valid_count(ch.len, e);
-                if (ACC) a[j] = load_f4<F>(acc + e, nv[j]);
+        for (int q = 0; q < CPB; ++q) {
+            const float* acc = ACC ? p.tensors[ch[q].tensor].acc + ch[q].start : nullptr;
+            const uint16_t* gp[kMaxGroup];
 #pragma unroll
-                for (int i = 0; i < NG; ++i) h[i][j] = load_h4<F>(gp[i] + e, nv[j]);
-            }
+            for (int i = 0; i < NG; ++i) gp[i] = g.set[i][ch[q].tensor] + ch[q].start;
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
+                const int e = lane_offset(j);
+                if (ACC) a[q][j] = load_f4<true>(acc + e, kGroup);
 #pragma unroll
-                for (int k = 0; k < kGroup; ++k) {
-                    uint32_t hk[kMaxGroup];
-                    element_terms<NG>(h, j, k, hk);
-                    const float gv = grad_sum<DT, ACC, NG>(ACC ? a[j].v[k] : 0.0f, hk, w) * inv;
-                    const double d = static_cast<double>(gv);
-                    // the square of an fp32 value is exact in binary64, so this
-                    // fma is the same as a rounded add of the exact square; the
-                    // zeros loaded for elements past the tail add exactly 0
-                    s = __builtin_fma(d, d, s);
+                for (int i = 0; i < NG; ++i) {
+                    const MPK_GLOBAL u32x2* x = (const MPK_GLOBAL u32x2*)(gp[i] + e);
+                    h[q][j][i] = MPK_NT_LOADS ? __builtin_nontemporal_load(x) : *x;
                 }
             }
-        });
+        }
+#pragma unroll
+        for (int q = 0; q < CPB; ++q)
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) add_squares<DT, ACC, NG>(a[q][j], h[q][j], w, inv, s);
+    } else {
+        for (int q = 0; q < CPB && c0 + q < p.n_chunks; ++q) {
+            const Chunk c = p.chunks[c0 + q];   // (ch[] is indexed by constants only)
+            const float* acc = ACC ? p.tensors[c.tensor].acc + c.start : nullptr;
+            const uint16_t* gp[kMaxGroup];
+#pragma unroll
+            for (int i = 0; i < NG; ++i) gp[i] = g.set[i][c.tensor] + c.start;
+            for_each_pass(c.len, [&](auto full, int base) {
+                constexpr bool F = decltype(full)::value;
+#pragma unroll
+                for (int j = 0; j < kGroupsPerLane; ++j) {
+                    const int e = base + lane_offset(j);
+                    const int nv = F ? kGroup : valid_count(c.len, e);
+                    const F4 a = ACC ? load_f4<F>(acc + e, nv) : F4{};
+                    u32x2 h[kMaxGroup];
+#pragma unroll
+                    for (int i = 0; i < NG; ++i) {
+                        const H4 x = load_h4<F>(gp[i] + e, nv);
+                        h[i][0] = x.v[0] | (x.v[1] << 16);
+                        h[i][1] = x.v[2] | (x.v[3] << 16);
+                    }
+                    add_squares<DT, ACC, NG>(a, h, w, inv, s);
+                }
+            });
+        }
     }
     const double total = block_sum(s);
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
@@ -535,7 +583,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
     const float b1 = a.beta1, b2 = a.beta2;
     const float ob1 = 1.0f - b1, ob2 = 1.0f - b2;
     const float eps = a.eps, lr = a.lr;
-    for (int64_t c = xcd_first_chunk(blockIdx.x, gridDim.x); c < p.n_chunks;
+    for (int64_t c = xcd_first_chunk<MPK_ADAMW_XCD_SPAN>(blockIdx.x, gridDim.x); c < p.n_chunks;
          c += gridDim.x) {
         const Chunk ch = p.chunks[c];
         const TensorDesc td = p.tensors[ch.tensor];
@@ -568,6 +616,9 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
             for (int j = 0; j < kGroupsPerLane; ++j) {
                 e[j] = base + lane_offset(j);
                 nv[j] = F ? kGroup : valid_count(ch.len, e[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < kGroupsPerLane; ++j) {
                 if (ACC) ga[j] = load_f4<F>(acc + e[j], nv[j]);
 #pragma unroll
                 for (int i = 0; i < NG; ++i) h[i][j] = load_h4<F>(gp[i] + e[j], nv[j]);
@@ -575,9 +626,9 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
                 m[j] = load_f4<F>(mm + e[j], nv[j]);
                 v[j] = load_f4<F>(mv + e[j], nv[j]);
             }
+            H4 out16[kGroupsPerLane];
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
-                H4 out16;
 #pragma unroll
                 for (int k = 0; k < kGroup; ++k) {
                     uint32_t hk[kMaxGroup];
@@ -595,12 +646,12 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
                     m[j].v[k] = mj;
                     v[j].v[k] = vj;
                     wv[j].v[k] = w;
-                    out16.v[k] = round16<DT>(w);
+                    out16[j].v[k] = round16<DT>(w);
                 }
                 store_f4<F>(mw + e[j], wv[j], nv[j]);
                 store_f4<F>(mm + e[j], m[j], nv[j]);
                 store_f4<F>(mv + e[j], v[j], nv[j]);
-                store_h4<F>(w16 + e[j], out16, nv[j]);
+                store_h4<F>(w16 + e[j], out16[j], nv[j]);
                 if (FP8 && codes != nullptr) {          // uniform over the block
                     const float scale = block16_scale(wv[j]);
                     if (F || nv[j] >= kGroup) {
@@ -830,14 +881,29 @@ hipError_t with_group(int dtype, const Grads& g, Fn&& fn)
 // With two 16-bit streams the lists disagreed (8B faster with 4 chunks, 1.3B
 // slower), and from 6 bytes per element up one chunk per block was fastest.
 // *used: the blocks launched, i.e. the number of first-stage partials.
+// Chunks per norm block: kNormChunks16 when the pass reads a single 16-bit
+// stream (no accumulator, one micro-batch), else kNormChunks.
+int norm_chunks_per_block(const Grads& g)
+{
+    return (!g.acc && g.n == 1) ? kNormChunks16 : kNormChunks;
+}
+
 hipError_t launch_norm_blocks(const PlanView& p, int grid, const Grads& g, int dtype,
                               double* partials, const DevState* st, hipStream_t s, int* used)
 {
     const int blocks = norm_blocks(grid, g);
     *used = blocks;
+    const bool single = norm_chunks_per_block(g) == kNormChunks16;
     return with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
-        k_norm_partial<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value>
-            <<<blocks, kBlock, 0, s>>>(p, g, st, partials);
+        constexpr int D = decltype(dt)::value, N = decltype(ng)::value;
+        constexpr bool A = decltype(acc)::value;
+        const unsigned lds = lds_for_blocks_per_cu(MPK_NORM_BLOCKS_PER_CU);
+        if (single) {
+            if constexpr (!A && N == 1)
+                k_norm_partial<D, A, N, kNormChunks16><<<blocks, kBlock, lds, s>>>(p, g, st, partials);
+        } else {
+            k_norm_partial<D, A, N, kNormChunks><<<blocks, kBlock, lds, s>>>(p, g, st, partials);
+        }
     });
 }
 
@@ -845,8 +911,8 @@ hipError_t launch_norm_blocks(const PlanView& p, int grid, const Grads& g, int d
 
 int norm_blocks(int grid, const Grads& g)
 {
-    if (!g.acc && g.n == 1) return grid / kNormChunks16 > 0 ? grid / kNormChunks16 : 1;
-    return grid;
+    const int cpb = norm_chunks_per_block(g);
+    return (grid + cpb - 1) / cpb;
 }
 
 hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int first, int dtype,
@@ -859,7 +925,7 @@ hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int fi
     return with_group(dtype, gg, [&](auto dt, auto acc, auto ng) {
         if constexpr (decltype(ng)::value > 0)
             k_accumulate<decltype(dt)::value, !decltype(acc)::value, decltype(ng)::value>
-                <<<grid, kBlock, 0, s>>>(p, gg);
+                <<<grid, kBlock, lds_for_blocks_per_cu(MPK_ACC_BLOCKS_PER_CU), s>>>(p, gg);
     });
 }
 
@@ -903,12 +969,13 @@ hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, 
         err = with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
             if constexpr (decltype(ng)::value <= 1)
                 k_adamw<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value, true>
-                    <<<grid, kBlock, 0, s>>>(p, g, a, fp8, st);
+                    <<<grid, kBlock, lds_for_blocks_per_cu(MPK_ADAMW_BLOCKS_PER_CU), s>>>(
+                        p, g, a, fp8, st);
         });
     } else {
         err = with_group(dtype, g, [&](auto dt, auto acc, auto ng) {
             k_adamw<decltype(dt)::value, decltype(acc)::value, decltype(ng)::value, false>
-                <<<grid, kBlock, 0, s>>>(p, g, a, fp8, st);
+                <<<grid, kBlock, lds_for_blocks_per_cu(MPK_ADAMW_BLOCKS_PER_CU), s>>>(p, g, a, fp8, st);
         });
     }
     if (err != hipSuccess) return err;
