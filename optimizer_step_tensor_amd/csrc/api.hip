@@ -25,6 +25,10 @@ struct Group {
     mpk::Weight w[mpk::kMaxGroup];
     int32_t n;
     int32_t no_acc;
+    // weights from token counts (mp_accumulate_first_counts), else NULL
+    const int64_t* counts;
+    float* weights_out;
+    int32_t k;
 };
 
 struct mp_plan {
@@ -276,6 +280,7 @@ mp_status check_group(const mp_plan* plan, const Group& g)
     for (int i = 0; i < g.n; ++i) {
         if (g.sets[i] == nullptr) return fail(MP_ERR_INVALID, "gradset %d of the group is NULL", i);
         if (g.sets[i]->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
+        if (g.counts != nullptr) continue;   // weights computed on the device from the counts
         mp_status st = check_weight(g.w[i], "a micro-batch weight");
         if (st != MP_OK) return st;
     }
@@ -326,6 +331,9 @@ mpk::Grads device_group(const Group& g)
     }
     d.n = g.n;
     d.acc = g.no_acc ? 0 : 1;
+    d.counts = g.counts;
+    d.weights_out = g.weights_out;
+    d.k = g.k;
     return d;
 }
 
@@ -822,9 +830,12 @@ mp_status accumulate(mp_plan* plan, const Group& g, int32_t first, mp_stream str
     return ok();
 }
 
-// partials: norm_blocks + kNormStage2 doubles of device scratch (NULL: the plan's)
+// partials: norm_blocks + kNormStage2 doubles of device scratch (NULL: the plan's).
+// tail.on: the whole update is enqueued by one call (update_step), so the norm's
+// finish also advances the clock and takes the scaler's decision.
 mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, float max_norm,
-                             mp_stream stream, double* partials = nullptr)
+                             mp_stream stream, double* partials = nullptr,
+                             mpk::Tail tail = mpk::Tail{})
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     mp_status st = check_group(plan, g);
@@ -834,7 +845,7 @@ mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, flo
     if (st != MP_OK) return st;
     hipError_t e = mpk::launch_norm(view(plan), plan->norm_grid, device_group(g), plan->dtype,
                                     partials != nullptr ? partials : plan->d_partials, max_norm,
-                                    state->d, static_cast<hipStream_t>(stream));
+                                    state->d, tail, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "norm launch");
     state->decision_pending = true;
     plan->partial_pending = false;
@@ -844,8 +855,11 @@ mp_status unscale_check_norm(mp_plan* plan, mp_state* state, const Group& g, flo
     return ok();
 }
 
+// with_scaler: the scaler's decision follows in the same tiny launch as the
+// clock; clock_advanced: both already ran in the norm's finish (update_step).
 mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_adamw_hparams* hp,
-                     const Fp8Out* fp8, mp_stream stream, bool with_scaler = false)
+                     const Fp8Out* fp8, mp_stream stream, bool with_scaler = false,
+                     bool clock_advanced = false)
 {
     if (plan == nullptr || state == nullptr) return fail(MP_ERR_INVALID, "plan and state are required");
     mp_status st = check_hparams(hp);
@@ -858,7 +872,8 @@ mp_status adamw_step(mp_plan* plan, mp_state* state, const Group& g, const mp_ad
                                   "no mp_gradset_update of them in between");
     st = check_devices(plan, state);
     if (st != MP_OK) return st;
-    mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    mpk::AdamArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay,
+                    clock_advanced ? 1 : 0};
     hipError_t e = mpk::launch_adamw(view(plan), plan->grid, device_group(g), plan->dtype, a, fp8,
                                      state->d, with_scaler, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "adamw launch");
@@ -889,8 +904,11 @@ mp_status update_step(mp_plan* plan, mp_state* state, const Group& g, float max_
         partials = scratch_of(plan->device, &e);
         if (partials == nullptr) return hip_fail(e, "scratch of mp_update_step_noalloc");
     }
-    st = unscale_check_norm(plan, state, g, max_norm, stream, partials);
-    if (st == MP_OK) st = adamw_step(plan, state, g, hp, nullptr, stream, true);
+    // the finish of the norm takes the clock and the scaler's decision (the tail):
+    // nothing else can run between the two passes of this call
+    st = unscale_check_norm(plan, state, g, max_norm, stream, partials,
+                            mpk::Tail{1, hp->beta1, hp->beta2});
+    if (st == MP_OK) st = adamw_step(plan, state, g, hp, nullptr, stream, true, true);
     return st;
 }
 
@@ -911,6 +929,28 @@ mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, cons
     mp_status st = make_group(sets, weights, n, weights_on_device, 1, &g);
     if (st != MP_OK) return st;
     return accumulate(plan, g, first, stream);
+}
+
+mp_status mp_accumulate_first_counts(mp_plan* plan, const mp_gradset* const* sets, int32_t n,
+                                     int32_t k, const int64_t* counts, float* weights_out,
+                                     mp_stream stream)
+{
+    if (sets == nullptr || counts == nullptr || weights_out == nullptr)
+        return fail(MP_ERR_INVALID, "sets, counts and weights_out are required");
+    if (n < 1 || n > mpk::kMaxGroup || k < n || k > mpk::kMaxCountsK)
+        return fail(MP_ERR_INVALID, "need 1 <= n <= %d and n <= k <= %d", mpk::kMaxGroup,
+                    mpk::kMaxCountsK);
+    if ((reinterpret_cast<uintptr_t>(counts) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(weights_out) & 3u) != 0)
+        return fail(MP_ERR_ALIGN, "counts must be 8-byte aligned, weights 4-byte aligned");
+    Group g{};
+    g.n = n;
+    g.no_acc = 1;
+    for (int i = 0; i < n; ++i) g.sets[i] = sets[i];
+    g.counts = counts;
+    g.weights_out = weights_out;
+    g.k = k;
+    return accumulate(plan, g, 1, stream);
 }
 
 mp_status mp_token_weights_dev(int32_t k, const int64_t* counts, float* weights_out,

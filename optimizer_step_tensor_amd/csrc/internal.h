@@ -89,6 +89,8 @@ constexpr int kBlock = 256;                          // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
 constexpr int kXcds = 8;                             // XCDs per MI355X
 constexpr int kNormStage2 = 256;                     // second-stage sums of the norm
+constexpr int kNormDirect = 8192;                    // at most this many partials: no second stage
+constexpr int kMaxCountsK = 64;                      // micro-batches of a pass that reads counts
 #ifndef MPK_NORM_CHUNKS
 #define MPK_NORM_CHUNKS 1          // consecutive chunks per norm block (several streams)
 #endif
@@ -136,6 +138,14 @@ struct PlanView {
 
 struct AdamArgs {
     float lr, beta1, beta2, eps, weight_decay;
+    int32_t clock_advanced;   // 1: the norm's finish already advanced the clock (Tail)
+};
+
+// The end of a whole update enqueued by one call: the norm's finishing block
+// also advances the optimizer clock and takes the scaler's decision.
+struct Tail {
+    int32_t on;
+    float beta1, beta2;
 };
 
 // A micro-batch weight n_i/N: a value passed with the launch or, when ptr is
@@ -159,6 +169,12 @@ struct Grads {
     Weight w[kMaxGroup];
     int32_t n;        // 0 .. kMaxGroup gradsets
     int32_t acc;      // 1: the accumulator is the first term
+    // token counts (or NULL): the weights of micro-batches 0..n-1 are computed
+    // from counts[0..k) by every block, and block 0 writes all k weights to
+    // weights_out (device memory) for the passes that follow
+    const int64_t* counts;
+    float* weights_out;
+    int32_t k;
 };
 
 // FP8 (E4M3) outputs of one tensor for the fused AdamW pass: numel codes and
@@ -175,7 +191,7 @@ hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int fi
 // `grid` blocks; the pass needs that many doubles plus kNormStage2 of scratch.
 int norm_blocks(int grid, const Grads& g);
 hipError_t launch_norm(const PlanView& p, int grid, const Grads& g, int dtype, double* partials,
-                       float max_norm, DevState* st, hipStream_t s);
+                       float max_norm, DevState* st, const Tail& tail, hipStream_t s);
 hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int dtype,
                                double* partials, const DevState* st, double* out, hipStream_t s);
 hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s);

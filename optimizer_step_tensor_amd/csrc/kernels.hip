@@ -213,10 +213,45 @@ __device__ __forceinline__ float grad_sum(float acc, const uint32_t (&h)[kMaxGro
     return x;
 }
 
-// The group's weights, each read once per block.
+// Token weights ("Accumulate gradients and recompute activations", "Weight each
+// mean by the targets it represents"): w_i = fp32(n_i / N) with N = sum of the k
+// counts, in binary64 then rounded once -- the host helper's arithmetic.  Counts
+// the host helper would refuse (n_i <= 0, N > 2^53) give NaN weights, so that the
+// step they feed overflows and is skipped.  Returns N, or -1 for refused counts.
+__device__ __forceinline__ double count_total(const int64_t* __restrict__ counts, int k)
+{
+    const int64_t limit = int64_t(1) << 53;
+    int64_t n = 0;
+    for (int i = 0; i < k; ++i) {              // in order, stopping the sum at the limit
+        const int64_t c = counts[i];
+        if (c <= 0 || c > limit - n) return -1.0;
+        n += c;
+    }
+    return static_cast<double>(n);
+}
+
+__device__ __forceinline__ float token_weight(const int64_t* __restrict__ counts, int i,
+                                              double total)
+{
+    return total > 0.0 ? static_cast<float>(static_cast<double>(counts[i]) / total)
+                       : __builtin_nanf("");
+}
+
+// The group's weights, each read once per block.  With token counts, every block
+// computes the weights of the first NG micro-batches itself, and block 0 also
+// writes all k weights to weights_out for the later passes.
 template <int NG>
 __device__ __forceinline__ void group_weights(const Grads& g, float (&w)[kMaxGroup])
 {
+    if (g.counts != nullptr) {
+        const double total = count_total(g.counts, g.k);
+#pragma unroll
+        for (int i = 0; i < kMaxGroup; ++i) w[i] = i < NG ? token_weight(g.counts, i, total) : 0.0f;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < g.k; i += kBlock)
+                g.weights_out[i] = token_weight(g.counts, i, total);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kMaxGroup; ++i) w[i] = i < NG ? weight_of(g.w[i]) : 0.0f;
 }
@@ -392,62 +427,77 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p, Grads g,
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
 }
 
+// Sum of x[lo..hi) by one block in a fixed order: lane t adds x[lo + t],
+// x[lo + t + 256], ... in increasing index (loads issued eight at a time), then
+// the block tree.  Valid in thread 0.
+__device__ __forceinline__ double block_sum_range(const double* __restrict__ x, int64_t lo,
+                                                  int64_t hi)
+{
+    double s = 0.0;
+    int64_t i = lo + threadIdx.x;
+    for (; i + 7 * kBlock < hi; i += 8 * kBlock) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = x[i + u * kBlock];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; i < hi; i += kBlock) s += x[i];
+    return block_sum(s);
+}
+
 // Second stage: block j sums the j-th of `gridDim.x` contiguous ranges of the n
-// first-stage partials, each lane a fixed strided subset, then the block tree.
+// first-stage partials.
 __global__ __launch_bounds__(kBlock) void k_norm_stage2(const double* __restrict__ partials,
                                                         int64_t n, double* __restrict__ out)
 {
     const int64_t per = (n + gridDim.x - 1) / gridDim.x;
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
     const int64_t hi = lo + per < n ? lo + per : n;
-    double s = 0.0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) s += partials[i];
-    const double total = block_sum(s);
+    const double total = block_sum_range(partials, lo, hi);
     if (threadIdx.x == 0) out[blockIdx.x] = total;
 }
 
-// Last stage: fixed-order sum of the second-stage sums, norm, clip coefficient
-// ("Megatron Internals III", section 9).
-__global__ __launch_bounds__(kBlock) void k_norm_finish(const double* __restrict__ partials,
-                                                        int n, float max_norm,
-                                                        DevState* __restrict__ st)
+// The optimizer clock advances only on a committed step ("Accumulate gradients
+// and recompute activations", "Discard a failed partial logical update").
+__device__ void advance_clock(DevState* __restrict__ st, float beta1, float beta2)
 {
-    double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += kBlock) s += partials[i];
-    const double total = block_sum(s);
-    if (threadIdx.x == 0) {
-        const int found_inf = !__builtin_isfinite(total);
-        const float norm = static_cast<float>(__builtin_sqrt(total));
-        float coef = 1.0f;
-        if (max_norm > 0.0f && !found_inf) {
-            const float q = max_norm / (norm + 1e-6f);
-            coef = q < 1.0f ? q : 1.0f;
+    if (st->s.found_inf) return;
+    st->s.step += 1;
+    st->s.beta1_pow = st->s.beta1_pow * static_cast<double>(beta1);
+    st->s.beta2_pow = st->s.beta2_pow * static_cast<double>(beta2);
+}
+
+// Dynamic loss-scale controller ("Mixed precision ...", section 2 "Dynamic
+// scaling"; "Megatron Internals III", section 5).
+__device__ void scaler_decision(DevState* __restrict__ st)
+{
+    const int found_inf = st->s.found_inf;
+    st->s.skipped = found_inf;
+    if (found_inf) st->s.skipped_total += 1;
+    if (!st->enabled) return;
+    float scale = st->s.scale;
+    if (found_inf) {
+        const float next = scale * st->backoff;
+        scale = next > st->min_scale ? next : st->min_scale;
+        st->s.good_steps = 0;
+    } else {
+        int good = st->s.good_steps + 1;
+        if (good == st->interval) {
+            const float next = scale * st->growth;
+            scale = next < st->max_scale ? next : st->max_scale;
+            good = 0;
         }
-        st->s.found_inf = found_inf;
-        st->s.sumsq = total;
-        st->s.grad_norm = norm;
-        st->s.clip_coef = coef;
-        st->update_scale = st->inv_scale * coef;
+        st->s.good_steps = good;
     }
+    st->s.scale = scale;
+    st->inv_scale = 1.0f / scale;
 }
 
-// The two halves of k_norm_finish, for a norm whose sum of squares is reduced
-// across ranks between them: this plan's fixed-order total, then the finish
-// from a (summed) total.
-__global__ __launch_bounds__(kBlock) void k_norm_reduce(const double* __restrict__ partials, int n,
-                                                        double* __restrict__ out)
+// Overflow flag, norm and clip coefficient from the total sum of squares
+// ("Megatron Internals III", section 9).
+__device__ void apply_norm(double total, float max_norm, DevState* __restrict__ st)
 {
-    double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += kBlock) s += partials[i];
-    const double total = block_sum(s);
-    if (threadIdx.x == 0) out[0] = total;
-}
-
-__global__ void k_norm_apply(const double* __restrict__ sumsq, float max_norm,
-                             DevState* __restrict__ st)
-{
-    if (threadIdx.x != 0) return;
-    const double total = sumsq[0];
     const int found_inf = !__builtin_isfinite(total);
     const float norm = static_cast<float>(__builtin_sqrt(total));
     float coef = 1.0f;
@@ -460,6 +510,36 @@ __global__ void k_norm_apply(const double* __restrict__ sumsq, float max_norm,
     st->s.grad_norm = norm;
     st->s.clip_coef = coef;
     st->update_scale = st->inv_scale * coef;
+}
+
+// Last stage: the fixed-order sum of n partial sums, then either the norm into
+// the state (out == NULL) or the total into *out.  With a tail (the whole
+// update enqueued by one call), the optimizer clock and the scaler's decision
+// follow in the same thread: both depend only on the overflow flag, and the
+// AdamW pass then reads the advanced clock.
+__global__ __launch_bounds__(kBlock) void k_norm_finish(const double* __restrict__ partials,
+                                                        int64_t n, float max_norm,
+                                                        DevState* __restrict__ st,
+                                                        double* __restrict__ out, Tail tail)
+{
+    const double total = block_sum_range(partials, 0, n);
+    if (threadIdx.x != 0) return;
+    if (out != nullptr) {
+        out[0] = total;
+        return;
+    }
+    apply_norm(total, max_norm, st);
+    if (tail.on) {
+        advance_clock(st, tail.beta1, tail.beta2);
+        scaler_decision(st);
+    }
+}
+
+// The finish from a sum of squares reduced across ranks.
+__global__ void k_norm_apply(const double* __restrict__ sumsq, float max_norm,
+                             DevState* __restrict__ st)
+{
+    if (threadIdx.x == 0) apply_norm(sumsq[0], max_norm, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,8 +658,12 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
     float gw[kMaxGroup];
     group_weights<NG>(g, gw);
     const float scale = st->update_scale;
-    const float bc1 = static_cast<float>(1.0 - st->s.beta1_pow * static_cast<double>(a.beta1));
-    const float bc2 = static_cast<float>(1.0 - st->s.beta2_pow * static_cast<double>(a.beta2));
+    // beta^(t+1): the clock advances after this pass, or (a.clock_advanced) the
+    // norm's finish already advanced it -- the same binary64 product either way
+    const double p1 = a.clock_advanced ? st->s.beta1_pow : st->s.beta1_pow * static_cast<double>(a.beta1);
+    const double p2 = a.clock_advanced ? st->s.beta2_pow : st->s.beta2_pow * static_cast<double>(a.beta2);
+    const float bc1 = static_cast<float>(1.0 - p1);
+    const float bc2 = static_cast<float>(1.0 - p2);
     const float b1 = a.beta1, b2 = a.beta2;
     const float ob1 = 1.0f - b1, ob2 = 1.0f - b2;
     const float eps = a.eps, lr = a.lr;
@@ -664,42 +748,6 @@ __global__ __launch_bounds__(kBlock) void k_adamw(PlanView p, Grads g, AdamArgs 
     }
 }
 
-// The optimizer clock advances only on a committed step ("Accumulate gradients
-// and recompute activations", "Discard a failed partial logical update").
-__device__ void advance_clock(DevState* __restrict__ st, float beta1, float beta2)
-{
-    if (st->s.found_inf) return;
-    st->s.step += 1;
-    st->s.beta1_pow = st->s.beta1_pow * static_cast<double>(beta1);
-    st->s.beta2_pow = st->s.beta2_pow * static_cast<double>(beta2);
-}
-
-// Dynamic loss-scale controller ("Mixed precision ...", section 2 "Dynamic
-// scaling"; "Megatron Internals III", section 5).
-__device__ void scaler_decision(DevState* __restrict__ st)
-{
-    const int found_inf = st->s.found_inf;
-    st->s.skipped = found_inf;
-    if (found_inf) st->s.skipped_total += 1;
-    if (!st->enabled) return;
-    float scale = st->s.scale;
-    if (found_inf) {
-        const float next = scale * st->backoff;
-        scale = next > st->min_scale ? next : st->min_scale;
-        st->s.good_steps = 0;
-    } else {
-        int good = st->s.good_steps + 1;
-        if (good == st->interval) {
-            const float next = scale * st->growth;
-            scale = next < st->max_scale ? next : st->max_scale;
-            good = 0;
-        }
-        st->s.good_steps = good;
-    }
-    st->s.scale = scale;
-    st->inv_scale = 1.0f / scale;
-}
-
 __global__ void k_adam_clock(DevState* __restrict__ st, float beta1, float beta2)
 {
     if (threadIdx.x == 0) advance_clock(st, beta1, beta2);
@@ -719,35 +767,12 @@ __global__ void k_clock_scaler(DevState* __restrict__ st, float beta1, float bet
     scaler_decision(st);
 }
 
-// Token weights on the device ("Accumulate gradients and recompute activations",
-// "Weight each mean by the targets it represents"): w_i = fp32(n_i / N) with
-// N = sum of the counts, in binary64 then rounded once -- the host helper's
-// arithmetic.  Counts the host helper would refuse (n_i <= 0, N > 2^53) give NaN
-// weights, so that the step they feed overflows and is skipped.
+// Token weights on the device (count_total, token_weight above).
 __global__ __launch_bounds__(kBlock) void k_token_weights(const int64_t* __restrict__ counts, int k,
                                                           float* __restrict__ weights)
 {
-    __shared__ double total;
-    __shared__ int valid;
-    if (threadIdx.x == 0) {
-        const int64_t limit = int64_t(1) << 53;
-        int64_t n = 0;
-        int ok = 1;
-        for (int i = 0; i < k; ++i) {              // in order, stopping the sum at the limit
-            const int64_t c = counts[i];
-            if (c <= 0 || c > limit - n) {
-                ok = 0;
-                break;
-            }
-            n += c;
-        }
-        total = static_cast<double>(n);
-        valid = ok;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < k; i += kBlock)
-        weights[i] = valid ? static_cast<float>(static_cast<double>(counts[i]) / total)
-                           : __builtin_nanf("");
+    const double total = count_total(counts, k);
+    for (int i = threadIdx.x; i < k; i += kBlock) weights[i] = token_weight(counts, i, total);
 }
 
 template <int DT>
@@ -929,16 +954,27 @@ hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int fi
     });
 }
 
+// After the first stage: up to kNormDirect partials are summed by the finishing
+// block itself, more go through kNormStage2 range sums first.
+hipError_t launch_norm_rest(double* partials, int np, float max_norm, DevState* st, double* out,
+                            const Tail& tail, hipStream_t s)
+{
+    if (np <= kNormDirect) {
+        k_norm_finish<<<1, kBlock, 0, s>>>(partials, np, max_norm, st, out, tail);
+    } else {
+        k_norm_stage2<<<kNormStage2, kBlock, 0, s>>>(partials, np, partials + np);
+        k_norm_finish<<<1, kBlock, 0, s>>>(partials + np, kNormStage2, max_norm, st, out, tail);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_norm(const PlanView& p, int grid, const Grads& g, int dtype, double* partials,
-                       float max_norm, DevState* st, hipStream_t s)
+                       float max_norm, DevState* st, const Tail& tail, hipStream_t s)
 {
     int np = 0;
     hipError_t err = launch_norm_blocks(p, grid, g, dtype, partials, st, s, &np);
     if (err != hipSuccess) return err;
-    const int n2 = np < kNormStage2 ? np : kNormStage2;
-    k_norm_stage2<<<n2, kBlock, 0, s>>>(partials, np, partials + np);
-    k_norm_finish<<<1, kBlock, 0, s>>>(partials + np, n2, max_norm, st);
-    return hipGetLastError();
+    return launch_norm_rest(partials, np, max_norm, st, nullptr, tail, s);
 }
 
 hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int dtype,
@@ -947,10 +983,7 @@ hipError_t launch_norm_partial(const PlanView& p, int grid, const Grads& g, int 
     int np = 0;
     hipError_t err = launch_norm_blocks(p, grid, g, dtype, partials, st, s, &np);
     if (err != hipSuccess) return err;
-    const int n2 = np < kNormStage2 ? np : kNormStage2;
-    k_norm_stage2<<<n2, kBlock, 0, s>>>(partials, np, partials + np);
-    k_norm_reduce<<<1, kBlock, 0, s>>>(partials + np, n2, out);
-    return hipGetLastError();
+    return launch_norm_rest(partials, np, 0.0f, nullptr, out, Tail{}, s);
 }
 
 hipError_t launch_norm_apply(const double* sumsq, float max_norm, DevState* st, hipStream_t s)
@@ -979,6 +1012,7 @@ hipError_t launch_adamw(const PlanView& p, int grid, const Grads& g, int dtype, 
         });
     }
     if (err != hipSuccess) return err;
+    if (a.clock_advanced) return hipSuccess;      // the norm's finish ran the tail
     if (with_scaler) k_clock_scaler<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
     else             k_adam_clock<<<1, 64, 0, s>>>(st, a.beta1, a.beta2);
     return hipGetLastError();
