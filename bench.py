@@ -53,11 +53,11 @@ def bytes_per_param(k):
 
 
 def launches_per_step(k, n_chunks, one_call):
-    """Kernel launches of one step as bench.py enqueues it: the accumulate passes (the token
-    weights inside the first, or their own launch when k = 1), the norm's first stage, its
-    second stage when there are more than 8192 partial sums, its finish, AdamW, then the clock
-    and the scaler (their own launches unless one call lets the finish take them)."""
-    n = (k - 1) if k > 1 else 1
+    """Kernel launches of one step as bench.py enqueues it: the token weights, the k - 1
+    accumulate passes, the norm's first stage, its second stage when there are more than 8192
+    partial sums, its finish, AdamW, then the clock and the scaler (their own launches unless
+    one call lets the norm's finish take them)."""
+    n = 1 + (k - 1)
     partials = n_chunks if k > 1 else (n_chunks + 15) // 16   # one stream: 16 chunks per block
     n += 1 + (1 if partials > 8192 else 0) + 1 + 1
     n += 0 if one_call else 2
@@ -554,10 +554,10 @@ def main():
     take = pool.pop
 
     def one_step_on(stream, record, one_call=False):
-        """One step.  The token weights come from the device counts inside the first
-        accumulation.  Eager steps call the norm, AdamW and the scaler separately, with events
-        around each; a captured step (one_call) enqueues them with mp_update_step_group, whose
-        norm finish also takes the clock and the scaler's decision (fewest launches)."""
+        """One step: the token weights from the device counts, the accumulations, then the norm,
+        AdamW and the scaler.  Eager steps call those three separately, with events around
+        each; a captured step (one_call) enqueues them with mp_update_step_group, whose norm
+        finish also takes the clock and the scaler's decision (fewest launches)."""
         def timed(name, fn):
             if record:
                 e0 = take()
@@ -571,16 +571,10 @@ def main():
         lif = int(k == 1)
         sp = ctypes.c_void_p(stream.cuda_stream)
         chk = mp._check
-        cptr, wdev = ctypes.c_void_p(counts_dev.data_ptr()), ctypes.c_void_p(weights_dev.data_ptr())
-        if k == 1:
-            chk(L.mp_token_weights_dev(k, cptr, wdev, sp))
+        chk(L.mp_token_weights_dev(k, counts_dev.data_ptr(), weights_dev.data_ptr(), sp))
         for i in range(k - 1):
-            if i == 0:
-                timed("accumulate", lambda: chk(L.mp_accumulate_first_counts(plan, one[0], 1, k, cptr,
-                                                                             wdev, sp)))
-            else:
-                timed("accumulate", lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1,
-                                                                          1, 0, sp)))
+            timed("accumulate", lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1, 1,
+                                                                      int(i == 0), sp)))
         if one_call:
             chk(L.mp_update_step_group(plan, state, one[-1], wptr[-1], 1, 1, lif, w.max_norm,
                                        ctypes.byref(hp), sp))
@@ -703,11 +697,10 @@ def main():
                    "kernel_events": "inside the timed region" if record else
                                     "eager steps after the timed graph replays",
                    "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
-                   "schedule": "k-1 accumulate passes (the first computing the token weights "
-                               "from device counts); the last micro-batch folded into the norm "
-                               "and AdamW passes" + ("; one call for norm + AdamW + scaler, whose "
-                                                     "norm finish takes the clock and the scaler"
-                                                     if args.graph else ""),
+                   "schedule": "token weights from device counts; k-1 accumulate passes; the "
+                               "last micro-batch folded into the norm and AdamW passes" +
+                               ("; one call for norm + AdamW + scaler, whose norm finish takes "
+                                "the clock and the scaler" if args.graph else ""),
                    "launches_per_step": launches_per_step(k, info["n_chunks"], args.graph),
                    "step_bytes_per_param": bpp["step"],
                    "step_GBps": step_bytes / ms_per_step / 1e6,

@@ -149,22 +149,6 @@ mp_status mp_token_weights(int32_t k, const int64_t* counts, float* weights_out)
 mp_status mp_token_weights_dev(int32_t k, const int64_t* counts, float* weights_out,
                                mp_stream stream);
 
-/* mp_token_weights_dev fused into the first accumulation of a logical update,
- * one launch instead of two: the same results, bit for bit, as
- *   mp_token_weights_dev(k, counts, weights_out);
- *   mp_accumulate_group(plan, sets, weights_out, n, 1, first = 1);
- * Every block of the pass computes the weights of micro-batches 0..n-1 from the
- * k counts itself (k int64 scalar reads), and one block writes all k weights to
- * weights_out, where the later passes of the update read them (group calls
- * with weights_on_device).  sets: the n gradsets of micro-batches 0..n-1 (host
- * array, 1 <= n <= 4); counts: k int64 in device memory (8-byte aligned,
- * n <= k <= 64); weights_out: k fp32 in device memory (4-byte aligned), both
- * owned by the caller.  Refused counts give NaN weights as in
- * mp_token_weights_dev.  Errors as mp_accumulate_group. */
-mp_status mp_accumulate_first_counts(mp_plan* plan, const mp_gradset* const* sets, int32_t n,
-                                     int32_t k, const int64_t* counts, float* weights_out,
-                                     mp_stream stream);
-
 /* Model-state bytes per parameter ("Chapter 41 Training at Scale", equation
  * (41.1)): 16-bit weight 2 + 16-bit gradient 2 + fp32 master 4 + m 4 + v 4 =
  * 16, plus 4 for the fp32 accumulation buffer when with_accumulator != 0.

@@ -77,6 +77,9 @@ namespace mpk {
 #ifndef MPK_ACC_BLOCKS_PER_CU
 #define MPK_ACC_BLOCKS_PER_CU 4
 #endif
+#ifndef MPK_ACC_FIRST_BLOCKS_PER_CU
+#define MPK_ACC_FIRST_BLOCKS_PER_CU 0   // the first accumulation (2 B read, 4 B written) lost
+#endif                                  // 20-30% with a cap of 3-6 on every list
 
 constexpr int kLdsPerCu = 160 * 1024;                // LDS of one gfx950 CU
 // Dynamic LDS bytes per block that let at most n blocks share a CU (n = 0: none).
@@ -90,7 +93,6 @@ constexpr int kWave = 64;
 constexpr int kXcds = 8;                             // XCDs per MI355X
 constexpr int kNormStage2 = 256;                     // second-stage sums of the norm
 constexpr int kNormDirect = 8192;                    // at most this many partials: no second stage
-constexpr int kMaxCountsK = 64;                      // micro-batches of a pass that reads counts
 #ifndef MPK_NORM_CHUNKS
 #define MPK_NORM_CHUNKS 1          // consecutive chunks per norm block (several streams)
 #endif
@@ -169,12 +171,6 @@ struct Grads {
     Weight w[kMaxGroup];
     int32_t n;        // 0 .. kMaxGroup gradsets
     int32_t acc;      // 1: the accumulator is the first term
-    // token counts (or NULL): the weights of micro-batches 0..n-1 are computed
-    // from counts[0..k) by every block, and block 0 writes all k weights to
-    // weights_out (device memory) for the passes that follow
-    const int64_t* counts;
-    float* weights_out;
-    int32_t k;
 };
 
 // FP8 (E4M3) outputs of one tensor for the fused AdamW pass: numel codes and

@@ -218,16 +218,22 @@ __device__ __forceinline__ float grad_sum(float acc, const uint32_t (&h)[kMaxGro
 // counts, in binary64 then rounded once -- the host helper's arithmetic.  Counts
 // the host helper would refuse (n_i <= 0, N > 2^53) give NaN weights, so that the
 // step they feed overflows and is skipped.  Returns N, or -1 for refused counts.
+// The running sum stops growing once a count is refused or the sum passes 2^53,
+// so it never leaves int64; the loads do not depend on it and can all be in
+// flight at once.
 __device__ __forceinline__ double count_total(const int64_t* __restrict__ counts, int k)
 {
     const int64_t limit = int64_t(1) << 53;
     int64_t n = 0;
-    for (int i = 0; i < k; ++i) {              // in order, stopping the sum at the limit
+    bool bad = false;
+#pragma unroll 8
+    for (int i = 0; i < k; ++i) {
         const int64_t c = counts[i];
-        if (c <= 0 || c > limit - n) return -1.0;
-        n += c;
+        bad |= c <= 0 || c > limit;
+        n += bad ? 0 : c;
+        bad |= n > limit;
     }
-    return static_cast<double>(n);
+    return bad ? -1.0 : static_cast<double>(n);
 }
 
 __device__ __forceinline__ float token_weight(const int64_t* __restrict__ counts, int i,
@@ -237,21 +243,10 @@ __device__ __forceinline__ float token_weight(const int64_t* __restrict__ counts
                        : __builtin_nanf("");
 }
 
-// The group's weights, each read once per block.  With token counts, every block
-// computes the weights of the first NG micro-batches itself, and block 0 also
-// writes all k weights to weights_out for the later passes.
+// The group's weights, each read once per block.
 template <int NG>
 __device__ __forceinline__ void group_weights(const Grads& g, float (&w)[kMaxGroup])
 {
-    if (g.counts != nullptr) {
-        const double total = count_total(g.counts, g.k);
-#pragma unroll
-        for (int i = 0; i < kMaxGroup; ++i) w[i] = i < NG ? token_weight(g.counts, i, total) : 0.0f;
-        if (blockIdx.x == 0)
-            for (int i = threadIdx.x; i < g.k; i += kBlock)
-                g.weights_out[i] = token_weight(g.counts, i, total);
-        return;
-    }
 #pragma unroll
     for (int i = 0; i < kMaxGroup; ++i) w[i] = i < NG ? weight_of(g.w[i]) : 0.0f;
 }
@@ -288,8 +283,10 @@ __device__ __forceinline__ double block_sum(double x)
 template <int DT, bool FIRST, int NG>
 __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p, Grads g)
 {
+    // the weights are read after a pass's loads are issued, so that a weight in
+    // device memory is read while the loads are in flight
     float w[kMaxGroup];
-    group_weights<NG>(g, w);
+    bool have_w = false;
     for (int64_t c = xcd_first_chunk<MPK_ACC_XCD_SPAN>(blockIdx.x, gridDim.x); c < p.n_chunks;
          c += gridDim.x) {
         const Chunk ch = p.chunks[c];
@@ -309,6 +306,10 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(PlanView p, Grads g)
 #pragma unroll
                 for (int i = 0; i < NG; ++i) h[i][j] = load_h4<F>(gp[i] + e[j], nv[j]);
                 if (!FIRST) a[j] = load_f4<F>(acc + e[j], nv[j]);
+            }
+            if (!have_w) {
+                group_weights<NG>(g, w);
+                have_w = true;
             }
 #pragma unroll
             for (int j = 0; j < kGroupsPerLane; ++j) {
@@ -950,7 +951,9 @@ hipError_t launch_accumulate(const PlanView& p, int grid, const Grads& g, int fi
     return with_group(dtype, gg, [&](auto dt, auto acc, auto ng) {
         if constexpr (decltype(ng)::value > 0)
             k_accumulate<decltype(dt)::value, !decltype(acc)::value, decltype(ng)::value>
-                <<<grid, kBlock, lds_for_blocks_per_cu(MPK_ACC_BLOCKS_PER_CU), s>>>(p, gg);
+                <<<grid, kBlock,
+                   lds_for_blocks_per_cu(first ? MPK_ACC_FIRST_BLOCKS_PER_CU : MPK_ACC_BLOCKS_PER_CU),
+                   s>>>(p, gg);
     });
 }
 

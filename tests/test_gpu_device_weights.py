@@ -179,44 +179,3 @@ def test_graph_replays_read_each_replays_counts(mp):
         eager.close()
         graphed.close()
 
-
-@pytest.mark.parametrize("n", [1, 2, 4])
-def test_first_accumulation_with_counts(mp, n):
-    """mp_accumulate_first_counts: one pass gives the bits of mp_token_weights_dev followed by
-    mp_accumulate_group(first=1) -- the weights it writes for the later passes and the
-    accumulator -- for valid counts and for refused ones (NaN weights, NaN accumulator)."""
-    import torch
-    import inputs
-    from harness import DeviceRun
-    w = configs.make("edges")
-    dev = DeviceRun(w, sep_grads=False)
-    extra = [dev.model.grad_buffers() for _ in range(n - 1)]
-    sets = [dev.gsets[0]] + [dev.model.gradset(g) for g in extra]
-    try:
-        for i, gl in enumerate([dev.g16[0]] + extra):
-            for t, x in enumerate(gl):
-                inputs.fill_dev_u16(x, w.grad_recipe(1, i, t), w.dtype)
-        for counts in ([451, 402, 509, 433, 500, 470][:max(n, 3)], [7] * 64, [4, 0, 5, 6][:max(n, 3)]):
-            k = len(counts)
-            c = torch.tensor(counts, dtype=torch.int64, device="cuda")
-            w_ref = torch.full((k,), 3.0, dtype=torch.float32, device="cuda")
-            mp.mp_token_weights_dev(k, c, w_ref)
-            mp.mp_accumulate_group(dev.model.plan, sets, w_ref.data_ptr(), True)
-            acc_ref = [a.cpu().numpy().copy() for a in dev.model.acc]
-            for a in dev.model.acc:
-                a.fill_(5.0)
-            w_got = torch.full((k,), 3.0, dtype=torch.float32, device="cuda")
-            mp.mp_accumulate_first_counts(dev.model.plan, sets, k, c, w_got)
-            acc_got = [a.cpu().numpy() for a in dev.model.acc]
-            assert np.array_equal(w_got.cpu().numpy().view(np.uint32),
-                                  w_ref.cpu().numpy().view(np.uint32)), counts
-            for a, b in zip(acc_got, acc_ref):
-                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), counts
-            say("  n=%d k=%d ok (weights %s)" % (n, k, w_got.cpu().numpy()[:3]))
-        with pytest.raises(mp.MpError) as e:                  # k out of range
-            mp.mp_accumulate_first_counts(dev.model.plan, sets, 65, c, w_got)
-        assert e.value.status == mp.MP_ERR_INVALID
-    finally:
-        for g in sets[1:]:
-            mp.mp_gradset_destroy(g)
-        dev.close()
