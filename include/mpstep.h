@@ -59,19 +59,29 @@ extern "C" {
 
 #define MPSTEP_ABI_VERSION 1
 
+/* The two enumerations span every int32 value (the _RANGE_ enumerators are not
+ * values of the ABI): a C caller may pass any int32 where one is expected, and
+ * the library refuses what is not a listed value without undefined behaviour. */
 typedef enum {
     MP_OK = 0,
     MP_ERR_INVALID = 1,   /* an argument is out of range or NULL */
     MP_ERR_ALIGN = 2,     /* a buffer is not 16-byte aligned */
     MP_ERR_NOMEM = 3,     /* a device or host allocation failed */
     MP_ERR_HIP = 4,       /* the HIP runtime reported an error */
-    MP_ERR_ORDER = 5      /* calls out of the documented order */
+    MP_ERR_ORDER = 5,     /* calls out of the documented order */
+    MP_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    MP_STATUS_RANGE_MAX_ = 2147483647
 } mp_status;
 
 /* The 16-bit model format ("Mixed precision ...", section 2, "Two 16-bit
  * formats"): bf16 = 8 significant bits and fp32's exponent range; fp16 = 11
  * significant bits, largest finite 65504, smallest subnormal 2^-24. */
-typedef enum { MP_BF16 = 0, MP_FP16 = 1 } mp_dtype16;
+typedef enum {
+    MP_BF16 = 0,
+    MP_FP16 = 1,
+    MP_DTYPE16_RANGE_MIN_ = -2147483647 - 1,
+    MP_DTYPE16_RANGE_MAX_ = 2147483647
+} mp_dtype16;
 
 typedef struct mp_plan mp_plan;        /* tensor list + chunk table (device) */
 typedef struct mp_gradset mp_gradset;  /* one micro-batch's gradient pointers (device) */

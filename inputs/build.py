@@ -18,9 +18,11 @@ def _run(cmd, out):
     return out
 
 
-def build_host():
+def build_host(sanitize=False):
+    """sanitize: AddressSanitizer + UndefinedBehaviorSanitizer, findings fatal (CPU test runs)."""
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-g"] if sanitize else []
     return _run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-                 "-fno-fast-math", "-Wall", "-o", "@OUT", os.path.join(HERE, "gen_host.c")],
+                 "-fno-fast-math", "-Wall", *san, "-o", "@OUT", os.path.join(HERE, "gen_host.c")],
                 HOST_LIB)
 
 

@@ -19,10 +19,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-I", os.path.join(ROOT, "include")]
 
 
-def build(out=LIB, extra=()):
+# The host half (argument checks, chunk tables, gradset slots) under AddressSanitizer
+# and UndefinedBehaviorSanitizer, findings fatal; the device code is built as usual.
+# For CPU test runs with clang's sanitizer runtime preloaded (tests/run_sanitized.py).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(out=LIB, extra=(), sanitize=False):
     """Compile the library (always recompiles); returns its path."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_HOST if sanitize else ()), *extra, "-o", tmp, *SOURCES]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

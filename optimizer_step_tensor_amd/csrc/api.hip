@@ -383,6 +383,7 @@ const char* mp_status_string(mp_status status)
     case MP_ERR_NOMEM: return "MP_ERR_NOMEM";
     case MP_ERR_HIP: return "MP_ERR_HIP";
     case MP_ERR_ORDER: return "MP_ERR_ORDER";
+    default: break;
     }
     return "MP_ERR_UNKNOWN";
 }

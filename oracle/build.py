@@ -15,10 +15,16 @@ CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Wextra"]
 
 
-def build(out=LIB, src=SRC, extra=()):
+# AddressSanitizer + UndefinedBehaviorSanitizer build, for a CPU test run with the
+# sanitizer runtime preloaded (tests/run_sanitized.py); every finding is fatal.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+            "-g"]
+
+
+def build(out=LIB, src=SRC, extra=(), sanitize=False):
     """Compile `src` into `out` (always recompiles); returns the library path."""
     tmp = out + ".tmp"
-    cmd = ["gcc", *CFLAGS, *extra, "-o", tmp, src, "-lm"]
+    cmd = ["gcc", *CFLAGS, *(SANITIZE if sanitize else ()), *extra, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

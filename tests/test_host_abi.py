@@ -126,7 +126,9 @@ def test_validation_before_any_device_work(mp):
     PP = ctypes.POINTER(ctypes.c_void_p)
     g = ctypes.cast(good, PP)
     assert L.mp_plan_create(0, ne, 0, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
-    assert L.mp_plan_create(1, ne, 7, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    for dt in (7, -5, 2 ** 31 - 1, -2 ** 31):             # any int32 is refused cleanly
+        assert L.mp_plan_create(1, ne, dt, None, g, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert mp.mp_status_string(99) == "MP_ERR_UNKNOWN" and mp.mp_status_string(-1) == "MP_ERR_UNKNOWN"
     assert L.mp_plan_create(1, ne, 0, None, None, g, g, g, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
     assert (L.mp_plan_create(1, ne, 0, None, ctypes.cast(bad, PP), g, g, g, None, ctypes.byref(out))
             == mp.MP_ERR_ALIGN)
