@@ -13,6 +13,26 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running (still part of the default suites)")
 
 
+@pytest.fixture
+def progress(capsys):
+    """A progress printer for long tests: each line goes past pytest's capture to the real
+    stdout (flushed) and into gpurun_out/test_progress.log, so that a long test is seen to
+    be alive while it runs."""
+    log_dir = os.path.join(ROOT, "gpurun_out")
+
+    def say(*a):
+        line = " ".join(str(x) for x in a)
+        with capsys.disabled():
+            print(line, flush=True)
+        try:
+            os.makedirs(log_dir, exist_ok=True)
+            with open(os.path.join(log_dir, "test_progress.log"), "a") as f:
+                f.write(line + "\n")
+        except OSError:
+            pass
+    return say
+
+
 @pytest.fixture(scope="session")
 def orc():
     import oracle

@@ -6,8 +6,6 @@ the oracle recomputes the global norm from regenerated inputs every step
 (streamed, all elements) and the update on sampled windows: the first and last
 512 elements of every tensor plus 64 seeded random windows of 4099 elements.
 """
-import sys
-
 import pytest
 
 from inputs import configs
@@ -15,15 +13,10 @@ from inputs import configs
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
 @pytest.mark.timeout(1100)
 @pytest.mark.parametrize("name,steps", [("ragged-4096", 2), ("llama3-8B", 2), ("huge-tensor", 2)])
-def test_full_size_sampled_parity(name, steps):
-    run_sampled_parity(name, steps)
+def test_full_size_sampled_parity(name, steps, progress):
+    run_sampled_parity(name, steps, say=progress)
 
 
 @pytest.mark.timeout(1100)
@@ -31,19 +24,19 @@ def test_full_size_sampled_parity(name, steps):
     ("llama3-8B", ([], [0, 1, 2, 3])),              # all four resident, no accumulator pass
     ("gpt-1.3B", ([[0, 1, 2, 3]], [4, 5, 6, 7])),   # four accumulated in one pass, four folded
 ])
-def test_full_size_resident_groups(name, schedule):
+def test_full_size_resident_groups(name, schedule, progress):
     """The group schedules bench.py times (extras.resident_groups), at full size, against the
     oracle's one-at-a-time steps on the same sampled windows and the full streamed norm."""
-    run_sampled_parity(name, 2, schedule=schedule)
+    run_sampled_parity(name, 2, schedule=schedule, say=progress)
 
 
 @pytest.mark.timeout(1100)
-def test_full_size_gpt13b_twenty_steps():
+def test_full_size_gpt13b_twenty_steps(progress):
     """The 1.3B list's stated run: 20 steps of k = 8 at full size, each checked."""
-    run_sampled_parity("gpt-1.3B", 20)
+    run_sampled_parity("gpt-1.3B", 20, say=progress)
 
 
-def run_sampled_parity(name, steps, schedule=None):
+def run_sampled_parity(name, steps, schedule=None, say=print):
     import torch
     from harness import DeviceRun, StreamedOracle, sample_windows, compare_windows
     assert torch.cuda.is_available()
