@@ -234,9 +234,9 @@ def time_ceiling(torch, w, model, g16_last, stream, kernel_ms, reps=3):
     """Bandwidth probes (optimizer_step_tensor_amd/csrc/ceiling.hip) over the model's own flat
     buffers, in the library's launch shape: the AdamW pass's exact traffic (5 streams read,
     4 written, trivial arithmetic, state left as it was) at several caps on resident blocks
-    per CU, the norm's read traffic, and a copy and a fill of the (dead) accumulator.  The
-    step's AdamW and norm launch times are rated against the fastest probe of their own
-    pattern."""
+    per CU, the norm's read traffic, the first and the later accumulations' traffic into the
+    (dead) accumulator, and a copy and a fill of it.  Each pass of the step is rated against
+    the fastest probe of its own pattern."""
     from optimizer_step_tensor_amd import build as lib_build
     if model.layout != "flat" or model.acc is None:
         return {"skipped": "needs the flat layout and an accumulator"}
@@ -246,7 +246,9 @@ def time_ceiling(torch, w, model, g16_last, stream, kernel_ms, reps=3):
     C.mpc_read_pattern.argtypes = [P_, P_, i64, P_, i32, i32, P_]
     C.mpc_copy_pattern.argtypes = [P_, P_, i64, i32, i32, P_]
     C.mpc_fill_pattern.argtypes = [P_, i64, f32, i32, i32, P_]
-    for f in (C.mpc_adamw_pattern, C.mpc_read_pattern, C.mpc_copy_pattern, C.mpc_fill_pattern):
+    C.mpc_accumulate_pattern.argtypes = [P_, P_, i64, i32, i32, i32, P_]
+    for f in (C.mpc_adamw_pattern, C.mpc_read_pattern, C.mpc_copy_pattern, C.mpc_fill_pattern,
+              C.mpc_accumulate_pattern):
         f.restype = i32
     (acc, master, m, v, w16, g), n = flat_extent(
         model, [model.acc, model.master, model.m, model.v, model.w16, g16_last])
@@ -288,12 +290,17 @@ def time_ceiling(torch, w, model, g16_last, stream, kernel_ms, reps=3):
                            "best_frac": best_rd["GBps"] / HBM_PEAK_GBPS}
     # the accumulator is dead between steps (the next first accumulation overwrites it)
     for name, fn, bpe in (
-            ("copy_in_place", lambda cap: C.mpc_copy_pattern(acc, acc, n, cap, 128, sp), 8),
-            ("fill", lambda cap: C.mpc_fill_pattern(acc, n, 0.0, cap, 128, sp), 4)):
+            ("first_accumulate_pattern",
+             lambda cap, span: C.mpc_accumulate_pattern(acc, g, n, 0, cap, span, sp), 6),
+            ("accumulate_pattern",
+             lambda cap, span: C.mpc_accumulate_pattern(acc, g, n, 1, cap, span, sp), 10),
+            ("copy_in_place", lambda cap, span: C.mpc_copy_pattern(acc, acc, n, cap, span, sp), 8),
+            ("fill", lambda cap, span: C.mpc_fill_pattern(acc, n, 0.0, cap, span, sp), 4)):
         runs = {}
         for cap in (0, 4):
-            ms = timed(lambda: fn(cap))
-            runs["cap%d" % cap] = {"ms": ms, "GBps": bpe * n / ms / 1e6}
+            for span in (64, 128):
+                ms = timed(lambda: fn(cap, span))
+                runs["cap%d_span%d" % (cap, span)] = {"ms": ms, "GBps": bpe * n / ms / 1e6}
         b = max(runs.values(), key=lambda r: r["GBps"])
         out[name] = {"bytes_per_element": bpe, "runs": runs, "best_GBps": b["GBps"],
                      "best_frac": b["GBps"] / HBM_PEAK_GBPS}
@@ -302,6 +309,11 @@ def time_ceiling(torch, w, model, g16_last, stream, kernel_ms, reps=3):
     step_norm = 6 * P / kernel_ms["norm"] / 1e6
     out["adamw_vs_pattern"] = step_adam / best["GBps"]
     out["norm_vs_pattern"] = step_norm / best_rd["GBps"]
+    out["first_accumulate_vs_pattern"] = (6 * P / kernel_ms["first_accumulate"] / 1e6 /
+                                          out["first_accumulate_pattern"]["best_GBps"])
+    if kernel_ms.get("accumulate"):
+        out["accumulate_vs_pattern"] = (10 * P / kernel_ms["accumulate"] / 1e6 /
+                                        out["accumulate_pattern"]["best_GBps"])
     # the fused step at the speed of its two patterns
     t_ceil = adam_bytes / best["GBps"] / 1e6 + read_bytes / best_rd["GBps"] / 1e6
     out["fused_step_pattern_frac"] = (adam_bytes + read_bytes) / t_ceil / 1e6 / HBM_PEAK_GBPS
@@ -543,7 +555,7 @@ def main():
         log("copy calibration: %d bytes read, %d bytes written" % (4 * n, 4 * n))
         del a, b
 
-    ev = {name: [] for name in ("accumulate", "norm", "adamw", "fused")}
+    ev = {name: [] for name in ("first_accumulate", "accumulate", "norm", "adamw", "fused")}
     # every timing event is created, and recorded once so that its HIP event exists, before
     # any timed region; the timed steps then only record them
     pool = [torch.cuda.Event(enable_timing=True)
@@ -574,8 +586,9 @@ def main():
         chk = mp._check
         chk(L.mp_token_weights_dev(k, counts_dev.data_ptr(), weights_dev.data_ptr(), sp))
         for i in range(k - 1):
-            timed("accumulate", lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1, 1,
-                                                                      int(i == 0), sp)))
+            timed("first_accumulate" if i == 0 else "accumulate",
+                  lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1, 1, int(i == 0),
+                                                        sp)))
         if one_call:
             chk(L.mp_update_step_group(plan, state, one[-1], wptr[-1], 1, 1, lif, w.max_norm,
                                        ctypes.byref(hp), sp))

@@ -151,6 +151,35 @@ __global__ __launch_bounds__(kBlock) void k_read_pattern(const float* acc, const
     if (s == 1.2345f) sink[blockIdx.x] = s;   // practically never: keeps the loads
 }
 
+// The accumulations' traffic.  First (acc = w * widen(g16)): read g16, write
+// acc.  Later (acc += w * widen(g16)): read acc and g16, write acc.  The
+// accumulator is dead between steps, so the probes may leave any finite value in it.
+template <bool LATER>
+__global__ __launch_bounds__(kBlock) void k_accumulate_pattern(float* acc, const uint16_t* g16,
+                                                               int64_t n, int span)
+{
+    const int64_t c = chunk_of(blockIdx.x, gridDim.x, span);
+    const int64_t base = c * kChunk;
+    f32x4 a[2];
+    u32x2 g[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t e = base + lane_elem(h);
+        if (!whole(e, n)) continue;
+        g[h] = ld2(g16 + e);
+        if (LATER) a[h] = ld4(acc + e);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t e = base + lane_elem(h);
+        if (!whole(e, n)) continue;
+        f32x4 x = {__uint_as_float(g[h].x << 16), __uint_as_float(g[h].x & 0xFFFF0000u),
+                   __uint_as_float(g[h].y << 16), __uint_as_float(g[h].y & 0xFFFF0000u)};
+        if (LATER) x = a[h] + x;
+        st4(acc + e, x);
+    }
+}
+
 // Plain copy (one fp32 read, one fp32 write) and fill (one fp32 write).
 __global__ __launch_bounds__(kBlock) void k_copy_pattern(const float* src, float* dst, int64_t n,
                                                          int span)
@@ -241,6 +270,21 @@ int mpc_read_pattern(const float* acc, const uint16_t* g16, int64_t n, float* si
     if (!aligned16(acc) || !aligned16(g16) || sink == nullptr) return 1;
     k_read_pattern<<<grid, kBlock, lds_bytes(blocks_per_cu), static_cast<hipStream_t>(stream)>>>(
         acc, g16, n, sink, span);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// later: 0 = the first accumulation's pattern, 1 = a later one's
+int mpc_accumulate_pattern(float* acc, const uint16_t* g16, int64_t n, int32_t later,
+                           int32_t blocks_per_cu, int32_t span, void* stream)
+{
+    unsigned grid;
+    if (!grid_of(n, &grid) || !shape_ok(blocks_per_cu, span)) return 1;
+    if (!aligned16(acc) || !aligned16(g16)) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (later)
+        k_accumulate_pattern<true><<<grid, kBlock, lds_bytes(blocks_per_cu), s>>>(acc, g16, n, span);
+    else
+        k_accumulate_pattern<false><<<grid, kBlock, lds_bytes(blocks_per_cu), s>>>(acc, g16, n, span);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

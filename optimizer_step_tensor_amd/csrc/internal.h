@@ -81,6 +81,18 @@ namespace mpk {
 #define MPK_ACC_FIRST_BLOCKS_PER_CU 0   // the first accumulation (2 B read, 4 B written) lost
 #endif                                  // 20-30% with a cap of 3-6 on every list
 
+// Descriptor tables and device-resident weights read through the constant
+// address space (scalar loads); 0: plain loads.  Timed in alternation, scalar
+// reads made the first accumulation 5-8% and the later ones (weights read on
+// the device) 8-9% faster on every list; AdamW's descriptor reads stay plain
+// (0-3% faster there).
+#ifndef MPK_SCALAR_TABLES
+#define MPK_SCALAR_TABLES 1
+#endif
+#ifndef MPK_ADAMW_SCALAR_TABLES
+#define MPK_ADAMW_SCALAR_TABLES 0
+#endif
+
 constexpr int kLdsPerCu = 160 * 1024;                // LDS of one gfx950 CU
 // Dynamic LDS bytes per block that let at most n blocks share a CU (n = 0: none).
 constexpr unsigned lds_for_blocks_per_cu(int n)

@@ -11,10 +11,13 @@ own plan over the same buffers; the numbers are medians over rounds.
 
     python -m optimizer_step_tensor_amd.tune build NAME=FLAGS [NAME=FLAGS ...]
     python -m optimizer_step_tensor_amd.tune time WORKLOAD NAME[,NAME...] [--rounds R] [--reps N]
+                                                   [--weights value|device]
 
 `build` runs on any machine with hipcc (FLAGS: comma-separated -D options, or
 empty for the defaults) and writes _build/tune/libmpstep_NAME.so; `time` needs
-the GPU and those files.  A timing run prints one markdown table.
+the GPU and those files.  A timing run prints one markdown table.  With
+--weights device every pass reads its micro-batch weight from device memory,
+as bench.py's step does; the default passes it as a launch argument.
 """
 import argparse
 import ctypes
@@ -41,7 +44,7 @@ def cmd_build(specs):
         print("built", name, " ".join(extra) or "(defaults)", flush=True)
 
 
-def cmd_time(workload, names, rounds, reps):
+def cmd_time(workload, names, rounds, reps, weights_on="value"):
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     import torch
@@ -63,6 +66,11 @@ def cmd_time(workload, names, rounds, reps):
     sp = ctypes.c_void_p(stream.cuda_stream)
     hp = mp.adamw_hparams(**w.hp)
     cfg = mp.scaler_cfg(init_scale=1.0, enabled=False)
+    on_dev = weights_on == "device"
+    wdev = torch.tensor([weights[0], weights[-1]], dtype=torch.float32, device="cuda")
+    whost = (ctypes.c_float * 2)(weights[0], weights[-1])
+    base = wdev.data_ptr() if on_dev else ctypes.addressof(whost)
+    wfirst, wlast = ctypes.c_void_p(base), ctypes.c_void_p(base + 4)
     libs = {}
     for n in names:
         L = mp._bind(ctypes.CDLL(variant_path(n)))
@@ -73,24 +81,25 @@ def cmd_time(workload, names, rounds, reps):
         assert L.mp_plan_create(N, ne, dt16, *ptrs, None, ctypes.byref(plan)) == 0
         assert L.mp_gradset_create(plan, mp._ptrs(g16), ctypes.byref(gs)) == 0
         assert L.mp_state_create(ctypes.byref(cfg), ctypes.byref(st)) == 0
-        libs[n] = (L, plan, gs, st)
+        libs[n] = (L, plan, (ctypes.c_void_p * 1)(gs.value), st)
     passes = ("first", "accumulate", "norm", "adamw")
     res = {n: {p: [] for p in passes} for n in names}
-    w0, wl = ctypes.c_float(weights[0]), ctypes.c_float(weights[-1])
+    d = int(on_dev)
     for r in range(rounds + 1):                       # round 0 warms up
         for n in names:
             L, plan, gs, st = libs[n]
             for _ in range(reps):
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
                 ev[0].record(stream)
-                assert L.mp_accumulate(plan, gs, w0, 1, sp) == 0
+                assert L.mp_accumulate_group(plan, gs, wfirst, 1, d, 1, sp) == 0
                 ev[1].record(stream)
-                assert L.mp_accumulate(plan, gs, w0, 0, sp) == 0
+                assert L.mp_accumulate_group(plan, gs, wfirst, 1, d, 0, sp) == 0
                 ev[2].record(stream)
-                assert L.mp_unscale_check_norm(plan, st, gs, wl, 0, ctypes.c_float(w.max_norm),
-                                               sp) == 0
+                assert L.mp_unscale_check_norm_group(plan, st, gs, wlast, 1, d, 0,
+                                                     ctypes.c_float(w.max_norm), sp) == 0
                 ev[3].record(stream)
-                assert L.mp_adamw_step(plan, st, gs, wl, 0, ctypes.byref(hp), sp) == 0
+                assert L.mp_adamw_step_group(plan, st, gs, wlast, 1, d, 0, ctypes.byref(hp),
+                                             sp) == 0
                 ev[4].record(stream)
                 assert L.mp_scaler_update(st, sp) == 0
                 torch.cuda.synchronize()
@@ -105,8 +114,8 @@ def cmd_time(workload, names, rounds, reps):
         cells = ["%.4g (%.0f)" % (med[p], bpp[p] * P / med[p] / 1e6) for p in passes]
         fused = 38 * P / (med["norm"] + med["adamw"]) / 1e6 / 8000 * 100
         print("| %s | %s | %.1f |" % (n, " | ".join(cells), fused), flush=True)
-    print("\n%s: %d parameters, medians of %d rounds x %d launches per pass" % (workload, P, rounds,
-                                                                              reps))
+    print("\n%s: %d parameters, medians of %d rounds x %d launches per pass, weights %s"
+          % (workload, P, rounds, reps, "read on the device" if on_dev else "as launch arguments"))
 
 
 def main():
@@ -119,11 +128,12 @@ def main():
     t.add_argument("names")
     t.add_argument("--rounds", type=int, default=4)
     t.add_argument("--reps", type=int, default=2)
+    t.add_argument("--weights", choices=("value", "device"), default="value")
     a = ap.parse_args()
     if a.cmd == "build":
         cmd_build(a.specs)
     else:
-        cmd_time(a.workload, a.names.split(","), a.rounds, a.reps)
+        cmd_time(a.workload, a.names.split(","), a.rounds, a.reps, a.weights)
 
 
 if __name__ == "__main__":
