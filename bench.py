@@ -1,8 +1,9 @@
 """Throughput of the fused mixed-precision update step on one MI355X.
 
 One step = one logical update of the whole hot path over one batch of synthetic
-input: token weights (on the device, from device-resident target counts),
-micro-batches 1..k-1 accumulated into the fp32 buffers, the last micro-batch
+input: micro-batches 1..k-1 accumulated into the fp32 buffers (the token
+weights computed from device-resident target counts inside the first of those
+passes), the last micro-batch
 folded into the unscale/overflow/norm pass and into the AdamW + RNE-cast pass,
 then the loss-scaler decision.  Inputs (fp32 masters,
 per-micro-batch bf16 gradients) are generated on the device before the timed
@@ -54,11 +55,12 @@ def bytes_per_param(k):
 
 
 def launches_per_step(k, n_chunks, one_call):
-    """Kernel launches of one step as bench.py enqueues it: the token weights, the k - 1
-    accumulate passes, the norm's first stage, its second stage when there are more than 8192
-    partial sums, its finish, AdamW, then the clock and the scaler (their own launches unless
-    one call lets the norm's finish take them)."""
-    n = 1 + (k - 1)
+    """Kernel launches of one step as bench.py enqueues it: the k - 1 accumulate passes (the
+    token weights computed inside the first, or their own launch when k = 1), the norm's first
+    stage, its second stage when there are more than 8192 partial sums, its finish, AdamW, then
+    the clock and the scaler (their own launches unless one call lets the norm's finish take
+    them)."""
+    n = (k - 1) if k > 1 else 1
     partials = n_chunks if k > 1 else (n_chunks + 15) // 16   # one stream: 16 chunks per block
     n += 1 + (1 if partials > 8192 else 0) + 1 + 1
     n += 0 if one_call else 2
@@ -541,6 +543,7 @@ def main():
     PP = ctypes.POINTER(ctypes.c_void_p)
     one = [ctypes.cast((ctypes.c_void_p * 1)(x.value), PP) for x in sets]   # groups of one
     wptr = [ctypes.c_void_p(weights_dev.data_ptr() + 4 * i) for i in range(k)]
+    cptr, wdev = ctypes.c_void_p(counts_dev.data_ptr()), ctypes.c_void_p(weights_dev.data_ptr())
     info = mp.mp_plan_info(plan)
     log("plan:", info, "| resident %.1f GB" % (torch.cuda.memory_allocated() / 1e9))
 
@@ -567,8 +570,8 @@ def main():
     take = pool.pop
 
     def one_step_on(stream, record, one_call=False):
-        """One step: the token weights from the device counts, the accumulations, then the norm,
-        AdamW and the scaler.  Eager steps call those three separately, with events around
+        """One step: the accumulations (the first computing the token weights from the device
+        counts, or their own launch when k = 1), then the norm, AdamW and the scaler.  Eager steps call those three separately, with events around
         each; a captured step (one_call) enqueues them with mp_update_step_group, whose norm
         finish also takes the clock and the scaler's decision (fewest launches)."""
         def timed(name, fn):
@@ -584,11 +587,15 @@ def main():
         lif = int(k == 1)
         sp = ctypes.c_void_p(stream.cuda_stream)
         chk = mp._check
-        chk(L.mp_token_weights_dev(k, counts_dev.data_ptr(), weights_dev.data_ptr(), sp))
+        if k == 1:
+            chk(L.mp_token_weights_dev(k, cptr, wdev, sp))
         for i in range(k - 1):
-            timed("first_accumulate" if i == 0 else "accumulate",
-                  lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1, 1, int(i == 0),
-                                                        sp)))
+            if i == 0:                        # the token weights are computed in this pass
+                timed("first_accumulate",
+                      lambda: chk(L.mp_accumulate_first_counts(plan, one[0], 1, k, cptr, wdev, sp)))
+            else:
+                timed("accumulate",
+                      lambda i=i: chk(L.mp_accumulate_group(plan, one[i], wptr[i], 1, 1, 0, sp)))
         if one_call:
             chk(L.mp_update_step_group(plan, state, one[-1], wptr[-1], 1, 1, lif, w.max_norm,
                                        ctypes.byref(hp), sp))
@@ -711,7 +718,8 @@ def main():
                    "kernel_events": "inside the timed region" if record else
                                     "eager steps after the timed graph replays",
                    "dtype16": "bf16" if w.dtype == inputs.BF16 else "fp16",
-                   "schedule": "token weights from device counts; k-1 accumulate passes; the "
+                   "schedule": "k-1 accumulate passes, the first computing the token weights "
+                               "from device counts; the "
                                "last micro-batch folded into the norm and AdamW passes" +
                                ("; one call for norm + AdamW + scaler, whose norm finish takes "
                                 "the clock and the scaler" if args.graph else ""),

@@ -276,6 +276,27 @@ mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, cons
                               int32_t n, int32_t weights_on_device, int32_t first,
                               mp_stream stream);
 
+/* The token weights ("Accumulate gradients and recompute activations", "Weight
+ * each mean by the targets it represents") computed inside the first
+ * accumulation of an update: one launch instead of two, with the same results,
+ * bit for bit, as
+ *   mp_token_weights_dev(k, counts, weights_out);
+ *   mp_accumulate_group(plan, sets, weights_out, n, 1, first = 1);
+ * Every block of the pass computes the weights of micro-batches 0..n-1 from
+ * the k counts itself (k int64 scalar reads), and one block writes all k
+ * weights to weights_out, where the later passes of the update read them
+ * (group calls with weights_on_device).
+ *   sets:        the n gradsets of micro-batches 0..n-1 (host array, 1 <= n <= 4);
+ *   counts:      k int64 in device memory (8-byte aligned), n <= k <= 64;
+ *   weights_out: k fp32 in device memory (4-byte aligned);
+ * both device arrays are the caller's.  Counts that mp_token_weights would
+ * refuse give NaN weights, as in mp_token_weights_dev.  MP_ERR_INVALID if n or
+ * k is out of range, a pointer is NULL, a gradset belongs to another plan or
+ * the plan has no accumulators; MP_ERR_ALIGN if a device array is misaligned. */
+mp_status mp_accumulate_first_counts(mp_plan* plan, const mp_gradset* const* sets, int32_t n,
+                                     int32_t k, const int64_t* counts, float* weights_out,
+                                     mp_stream stream);
+
 /* Unscale, check and measure ("Megatron Internals III", sections 4, 6 and 9;
  * "Mixed precision ...", section 2 "Dynamic scaling").  The gradient of each
  * element is g_eff = acc (last == NULL), fl(w_last * widen(last))

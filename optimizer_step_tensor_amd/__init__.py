@@ -33,7 +33,7 @@ ENTRY_POINTS = [
     "mp_cast_fp8_blocks", "mp_fp8set_create", "mp_fp8set_destroy", "mp_adamw_step_fp8",
     "mp_gradset_update", "mp_update_step", "mp_token_weights_dev", "mp_accumulate_group",
     "mp_update_step_group", "mp_unscale_check_norm_group", "mp_adamw_step_group",
-    "mp_norm_partial_group", "mp_update_step_noalloc",
+    "mp_norm_partial_group", "mp_update_step_noalloc", "mp_accumulate_first_counts",
 ]
 
 MP_STATE_BLOB_BYTES = 256
@@ -125,6 +125,7 @@ def _bind(L):
                                    i32),
         "mp_token_weights_dev": ([i32, P, P, P], i32),
         "mp_accumulate_group": ([P, PP, P, i32, i32, i32, P], i32),
+        "mp_accumulate_first_counts": ([P, PP, i32, i32, P, P, P], i32),
         "mp_update_step_group": ([P, P, PP, P, i32, i32, i32, f32, ctypes.POINTER(AdamWHparams),
                                   P], i32),
         "mp_unscale_check_norm_group": ([P, P, PP, P, i32, i32, i32, f32, P], i32),
@@ -302,6 +303,16 @@ def mp_accumulate_group(plan, sets, weights, first, stream=None):
     arr, w, dev = _group(sets, weights)
     _check(lib().mp_accumulate_group(plan, arr, w, len(sets), dev, int(bool(first)),
                                      _stream(stream)))
+
+
+def mp_accumulate_first_counts(plan, sets, k, counts, weights_out, stream=None):
+    """Token weights from device counts computed inside the first accumulation of sets (see
+    the header); weights_out receives all k weights for the later passes."""
+    arr = (ctypes.c_void_p * len(sets))(*[x.value if isinstance(x, ctypes.c_void_p) else x
+                                          for x in sets])
+    _check(lib().mp_accumulate_first_counts(plan, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+                                            len(sets), int(k), _addr(counts), _addr(weights_out),
+                                            _stream(stream)))
 
 
 def mp_unscale_check_norm(plan, state, last, w_last, last_is_first, max_norm, stream=None):

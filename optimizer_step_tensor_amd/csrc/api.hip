@@ -25,6 +25,10 @@ struct Group {
     mpk::Weight w[mpk::kMaxGroup];
     int32_t n;
     int32_t no_acc;
+    // weights from token counts (mp_accumulate_first_counts), else NULL
+    const int64_t* counts;
+    float* weights_out;
+    int32_t k;
 };
 
 struct mp_plan {
@@ -276,6 +280,7 @@ mp_status check_group(const mp_plan* plan, const Group& g)
     for (int i = 0; i < g.n; ++i) {
         if (g.sets[i] == nullptr) return fail(MP_ERR_INVALID, "gradset %d of the group is NULL", i);
         if (g.sets[i]->plan != plan) return fail(MP_ERR_INVALID, "gradset belongs to another plan");
+        if (g.counts != nullptr) continue;   // weights computed on the device from the counts
         mp_status st = check_weight(g.w[i], "a micro-batch weight");
         if (st != MP_OK) return st;
     }
@@ -326,6 +331,9 @@ mpk::Grads device_group(const Group& g)
     }
     d.n = g.n;
     d.acc = g.no_acc ? 0 : 1;
+    d.counts = g.counts;
+    d.weights_out = g.weights_out;
+    d.k = g.k;
     return d;
 }
 
@@ -922,6 +930,28 @@ mp_status mp_accumulate_group(mp_plan* plan, const mp_gradset* const* sets, cons
     mp_status st = make_group(sets, weights, n, weights_on_device, 1, &g);
     if (st != MP_OK) return st;
     return accumulate(plan, g, first, stream);
+}
+
+mp_status mp_accumulate_first_counts(mp_plan* plan, const mp_gradset* const* sets, int32_t n,
+                                     int32_t k, const int64_t* counts, float* weights_out,
+                                     mp_stream stream)
+{
+    if (sets == nullptr || counts == nullptr || weights_out == nullptr)
+        return fail(MP_ERR_INVALID, "sets, counts and weights_out are required");
+    if (n < 1 || n > mpk::kMaxGroup || k < n || k > mpk::kMaxCountsK)
+        return fail(MP_ERR_INVALID, "need 1 <= n <= %d and n <= k <= %d", mpk::kMaxGroup,
+                    mpk::kMaxCountsK);
+    if ((reinterpret_cast<uintptr_t>(counts) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(weights_out) & 3u) != 0)
+        return fail(MP_ERR_ALIGN, "counts must be 8-byte aligned, weights 4-byte aligned");
+    Group g{};
+    g.n = n;
+    g.no_acc = 1;
+    for (int i = 0; i < n; ++i) g.sets[i] = sets[i];
+    g.counts = counts;
+    g.weights_out = weights_out;
+    g.k = k;
+    return accumulate(plan, g, 1, stream);
 }
 
 mp_status mp_token_weights_dev(int32_t k, const int64_t* counts, float* weights_out,

@@ -105,6 +105,7 @@ constexpr int kWave = 64;
 constexpr int kXcds = 8;                             // XCDs per MI355X
 constexpr int kNormStage2 = 256;                     // second-stage sums of the norm
 constexpr int kNormDirect = 8192;                    // at most this many partials: no second stage
+constexpr int kMaxCountsK = 64;                      // micro-batches of a pass that reads counts
 #ifndef MPK_NORM_CHUNKS
 #define MPK_NORM_CHUNKS 1          // consecutive chunks per norm block (several streams)
 #endif
@@ -183,6 +184,12 @@ struct Grads {
     Weight w[kMaxGroup];
     int32_t n;        // 0 .. kMaxGroup gradsets
     int32_t acc;      // 1: the accumulator is the first term
+    // The first accumulation with its weights computed from the k token counts
+    // (device int64[k], k <= kMaxCountsK) instead of w[]; block 0 writes all k
+    // weights to weights_out (device float[k]).  NULL counts: the weights are w[].
+    const int64_t* counts;
+    float* weights_out;
+    int32_t k;
 };
 
 // FP8 (E4M3) outputs of one tensor for the fused AdamW pass: numel codes and

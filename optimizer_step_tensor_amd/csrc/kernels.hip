@@ -258,7 +258,7 @@ __device__ __forceinline__ double count_total(const int64_t* __restrict__ counts
     bool bad = false;
 #pragma unroll 8
     for (int i = 0; i < k; ++i) {
-        const int64_t c = counts[i];
+        const int64_t c = read_table(counts + i);
         bad |= c <= 0 || c > limit;
         n += bad ? 0 : c;
         bad |= n > limit;
@@ -269,14 +269,27 @@ __device__ __forceinline__ double count_total(const int64_t* __restrict__ counts
 __device__ __forceinline__ float token_weight(const int64_t* __restrict__ counts, int i,
                                               double total)
 {
-    return total > 0.0 ? static_cast<float>(static_cast<double>(counts[i]) / total)
+    return total > 0.0 ? static_cast<float>(static_cast<double>(read_table(counts + i)) / total)
                        : __builtin_nanf("");
 }
 
-// The group's weights, each read once per block.
+// The group's weights, each read once per block.  With token counts (the first
+// accumulation of an update), every block computes the weights of micro-batches
+// 0..NG-1 from the k counts itself, and block 0 also writes all k weights to
+// weights_out, where the later passes of the update read them.
 template <int NG>
 __device__ __forceinline__ void group_weights(const Grads& g, float (&w)[kMaxGroup])
 {
+    if (g.counts != nullptr) {
+        const double total = count_total(g.counts, g.k);
+#pragma unroll
+        for (int i = 0; i < kMaxGroup; ++i)
+            w[i] = i < NG ? token_weight(g.counts, i, total) : 0.0f;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < g.k; i += kBlock)
+                g.weights_out[i] = token_weight(g.counts, i, total);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kMaxGroup; ++i) w[i] = i < NG ? weight_of(g.w[i]) : 0.0f;
 }
@@ -461,21 +474,25 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(PlanView p, Grads g,
 }
 
 // Sum of x[lo..hi) by one block in a fixed order: lane t adds x[lo + t],
-// x[lo + t + 256], ... in increasing index (loads issued eight at a time), then
-// the block tree.  Valid in thread 0.
+// x[lo + t + 256], ... in increasing index, then the block tree.  Valid in
+// thread 0.  The loads are issued 32 at a time, those past hi replaced by
+// +0.0, which leaves a sum of squares (>= +0, inf or NaN) exactly as it was:
+// up to 8192 partials cost one memory latency instead of a chain of them.
+constexpr int kSumBatch = 32;
 __device__ __forceinline__ double block_sum_range(const double* __restrict__ x, int64_t lo,
                                                   int64_t hi)
 {
     double s = 0.0;
-    int64_t i = lo + threadIdx.x;
-    for (; i + 7 * kBlock < hi; i += 8 * kBlock) {
-        double v[8];
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kSumBatch * kBlock) {
+        double v[kSumBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = x[i + u * kBlock];
+        for (int u = 0; u < kSumBatch; ++u) {
+            const int64_t j = i + static_cast<int64_t>(u) * kBlock;
+            v[u] = j < hi ? x[j] : 0.0;
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < kSumBatch; ++u) s += v[u];
     }
-    for (; i < hi; i += kBlock) s += x[i];
     return block_sum(s);
 }
 

@@ -179,3 +179,60 @@ def test_graph_replays_read_each_replays_counts(mp):
         eager.close()
         graphed.close()
 
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_first_accumulation_with_counts(mp, n):
+    """mp_accumulate_first_counts: one pass gives the bits of mp_token_weights_dev followed by
+    mp_accumulate_group(first=1) -- the weights it writes for the later passes (equal to the
+    oracle's) and the accumulator -- for valid counts, for the largest k, and for counts the
+    host would refuse (NaN weights, NaN accumulator)."""
+    import torch
+    import inputs
+    from harness import DeviceRun
+    w = configs.make("edges")
+    dev = DeviceRun(w, sep_grads=False)
+    extra = [dev.model.grad_buffers() for _ in range(n - 1)]
+    sets = [dev.gsets[0]] + [dev.model.gradset(g) for g in extra]
+    try:
+        for i, gl in enumerate([dev.g16[0]] + extra):
+            for t, x in enumerate(gl):
+                inputs.fill_dev_u16(x, w.grad_recipe(1, i, t), w.dtype)
+        valid = [451, 402, 509, 433, 500, 470][:max(n, 3)]
+        for counts in (valid, [7] * 64, [4, 0, 5, 6][:max(n, 3)]):
+            k = len(counts)
+            c = torch.tensor(counts, dtype=torch.int64, device="cuda")
+            w_ref = torch.full((k,), 3.0, dtype=torch.float32, device="cuda")
+            mp.mp_token_weights_dev(k, c, w_ref)
+            mp.mp_accumulate_group(dev.model.plan, sets, w_ref.data_ptr(), True)
+            acc_ref = [a.cpu().numpy().copy() for a in dev.model.acc]
+            for a in dev.model.acc:
+                a.fill_(5.0)
+            w_got = torch.full((k,), 3.0, dtype=torch.float32, device="cuda")
+            mp.mp_accumulate_first_counts(dev.model.plan, sets, k, c, w_got)
+            acc_got = [a.cpu().numpy() for a in dev.model.acc]
+            got = w_got.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), w_ref.cpu().numpy().view(np.uint32)), counts
+            if 0 not in counts:
+                want = np.asarray(oracle.token_weights(counts), dtype=np.float32)
+                assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), counts
+            else:
+                assert np.isnan(got).all() and all(np.isnan(a).all() for a in acc_got)
+            for a, b in zip(acc_got, acc_ref):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), counts
+            say("  n=%d k=%d ok (weights %s)" % (n, k, got[:3]))
+        c = torch.ones(65, dtype=torch.int64, device="cuda")
+        w_got = torch.empty(65, dtype=torch.float32, device="cuda")
+        with pytest.raises(mp.MpError) as e:                  # k out of range
+            mp.mp_accumulate_first_counts(dev.model.plan, sets, 65, c, w_got)
+        assert e.value.status == mp.MP_ERR_INVALID
+        with pytest.raises(mp.MpError) as e:                  # fewer counts than gradsets
+            mp.mp_accumulate_first_counts(dev.model.plan, sets, n - 1, c, w_got)
+        assert e.value.status == mp.MP_ERR_INVALID
+        with pytest.raises(mp.MpError) as e:                  # misaligned counts
+            mp.mp_accumulate_first_counts(dev.model.plan, sets, n, c.data_ptr() + 4, w_got)
+        assert e.value.status == mp.MP_ERR_ALIGN
+    finally:
+        for g in sets[1:]:
+            mp.mp_gradset_destroy(g)
+        dev.close()
