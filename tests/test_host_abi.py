@@ -200,6 +200,17 @@ def test_validation_before_any_device_work(mp):
                                         ctypes.c_void_p(0x10000), None) == mp.MP_ERR_INVALID)
     assert (L.mp_norm_partial_group(None, None, two, wts, 1, 0, 0, ctypes.c_void_p(0x10000), None)
             == mp.MP_ERR_INVALID)
+    # the first accumulation with counts: NULL arrays, n and k ranges, alignment (the plan is
+    # not touched before these)
+    fc = L.mp_accumulate_first_counts
+    assert fc(fake_state, None, 1, 4, dev, dev, None) == mp.MP_ERR_INVALID
+    assert fc(fake_state, two, 1, 4, None, dev, None) == mp.MP_ERR_INVALID
+    assert fc(fake_state, two, 1, 4, dev, None, None) == mp.MP_ERR_INVALID
+    for n, k in ((0, 4), (5, 8), (2, 1), (1, 65), (1, 0)):
+        assert fc(fake_state, two, n, k, dev, dev, None) == mp.MP_ERR_INVALID, (n, k)
+    assert fc(fake_state, two, 1, 4, ctypes.c_void_p(0x10004), dev, None) == mp.MP_ERR_ALIGN
+    assert fc(fake_state, two, 1, 4, dev, ctypes.c_void_p(0x10002), None) == mp.MP_ERR_ALIGN
+    assert fc(None, two, 1, 4, dev, dev, None) == mp.MP_ERR_INVALID
 
 
 def test_bench_refuses_more_than_one_gpu():
