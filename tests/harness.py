@@ -100,6 +100,10 @@ class DeviceRun:
         self.device_weights = False        # True: weights from device counts, steps use the
         self.dev_counts = None             # group entry points (kept alive until the next step)
         self.dev_weights = None
+        self.first_counts = False          # with device_weights: the weights computed inside the
+                                           # first accumulation (mp_accumulate_first_counts)
+        self.separate = False              # with device_weights: norm, AdamW and scaler as three
+                                           # group calls instead of mp_update_step_group
         # (accumulate groups, folded group) of micro-batch indices: steps use
         # mp_accumulate_group per group, then mp_update_step_group on the folded one
         self.schedule = None
@@ -183,22 +187,36 @@ class DeviceRun:
         return None
 
     def _step_device_weights(self, s, snapshot):
-        """The step with n_i in device memory: mp_token_weights_dev, then the one-micro-batch
-        group calls, which read each weight where the kernels run."""
+        """The step with n_i in device memory: the weights from mp_token_weights_dev or, with
+        first_counts, computed inside the first accumulation; then the one-micro-batch group
+        calls, which read each weight where the kernels run.  first_counts and separate
+        together are bench.py's eager step, first_counts alone its captured one."""
         torch, mp, w = self.torch, self.mp, self.w
+        plan = self.model.plan
         self.dev_counts = torch.tensor(w.token_counts(s), dtype=torch.int64, device="cuda")
         self.dev_weights = torch.empty(w.k, dtype=torch.float32, device="cuda")
-        mp.mp_token_weights_dev(w.k, self.dev_counts, self.dev_weights)
         wp = [self.dev_weights.data_ptr() + 4 * i for i in range(w.k)]
         n_acc = w.k if not self.fold_last else w.k - 1
+        in_first = self.first_counts and n_acc >= 1
+        if not in_first:
+            mp.mp_token_weights_dev(w.k, self.dev_counts, self.dev_weights)
         for i in range(n_acc):
-            mp.mp_accumulate_group(self.model.plan, [self.gsets[i]], wp[i], i == 0)
+            if i == 0 and in_first:
+                mp.mp_accumulate_first_counts(plan, [self.gsets[0]], w.k, self.dev_counts,
+                                              self.dev_weights)
+            else:
+                mp.mp_accumulate_group(plan, [self.gsets[i]], wp[i], i == 0)
         acc_snapshot = ([a.cpu().numpy() for a in self.model.acc]
                         if snapshot and self.model.acc is not None else None)
         if not self.fold_last:
-            mp.mp_update_step(self.model.plan, self.state, None, 1.0, 0, w.max_norm, self.hp)
+            mp.mp_update_step(plan, self.state, None, 1.0, 0, w.max_norm, self.hp)
+        elif self.separate:
+            last, lif = [self.gsets[w.k - 1]], w.k == 1
+            mp.mp_unscale_check_norm_group(plan, self.state, last, wp[-1], lif, w.max_norm)
+            mp.mp_adamw_step_group(plan, self.state, last, wp[-1], lif, self.hp)
+            mp.mp_scaler_update(self.state)
         else:
-            mp.mp_update_step_group(self.model.plan, self.state, [self.gsets[w.k - 1]], wp[-1],
+            mp.mp_update_step_group(plan, self.state, [self.gsets[w.k - 1]], wp[-1],
                                     w.k == 1, w.max_norm, self.hp)
         return acc_snapshot
 

@@ -61,18 +61,25 @@ def test_refused_counts_give_nan_weights(mp):
         assert np.isnan(got).all(), counts
 
 
-@pytest.mark.parametrize("name,fold_last", [("edges-fp16", True), ("llama-10.5M", True),
-                                            ("edges", False)])
-def test_device_weight_steps_equal_the_oracle(mp, name, fold_last):
-    """Steps driven by mp_token_weights_dev and one-micro-batch group calls reading the weights on
-    the device (mp_accumulate_group, mp_update_step_group) equal the oracle's, through the fp16
-    list's overflow and change of S."""
+@pytest.mark.parametrize("name,fold_last,sequence", [
+    ("edges-fp16", True, "weights_dev"), ("llama-10.5M", True, "weights_dev"),
+    ("edges", False, "weights_dev"),
+    ("edges-fp16", True, "bench_eager"), ("llama-10.5M", True, "bench_eager"),
+    ("llama-10.5M", True, "bench_graph"), ("edges", False, "counts_in_first")])
+def test_device_weight_steps_equal_the_oracle(mp, name, fold_last, sequence):
+    """Steps whose weights come from device counts equal the oracle's, through the fp16 list's
+    overflow and change of S: weights from mp_token_weights_dev, or computed inside the first
+    accumulation (mp_accumulate_first_counts); then one-micro-batch group calls reading them on
+    the device -- mp_update_step_group, or (bench_eager, bench.py's eager step) the norm, AdamW
+    and scaler as three calls."""
     from harness import OracleRun, DeviceRun, compare_step
     w = configs.make(name)
     orc = OracleRun(w)
     dev = DeviceRun(w)
     orc.fold_last = dev.fold_last = fold_last
     dev.device_weights = True
+    dev.first_counts = sequence != "weights_dev"
+    dev.separate = sequence == "bench_eager"
     try:
         for s in range(1, w.steps + 1):
             scale = orc.st.scaler.scale
@@ -83,10 +90,12 @@ def test_device_weight_steps_equal_the_oracle(mp, name, fold_last):
         dev.close()
 
 
-def test_refused_counts_skip_the_step(mp):
+@pytest.mark.parametrize("in_first", [False, True])
+def test_refused_counts_skip_the_step(mp, in_first):
     """A count of zero on the device makes the weights NaN, so the step is skipped exactly as an
     overflow is ("Discard a failed partial logical update"): no master, moment or 16-bit weight
-    changes, the clock stays, and the scaler backs off."""
+    changes, the clock stays, and the scaler backs off -- with the weights from
+    mp_token_weights_dev or computed inside the first accumulation."""
     import torch
     from harness import DeviceRun
     w = configs.make("edges-fp16")
@@ -100,10 +109,14 @@ def test_refused_counts_skip_the_step(mp):
         dev.fill_grads(2, before["scale"])
         cnt = torch.tensor([0] + [5] * (w.k - 1), dtype=torch.int64, device="cuda")
         wts = torch.empty(w.k, dtype=torch.float32, device="cuda")
-        mp.mp_token_weights_dev(w.k, cnt, wts)
         plan = dev.model.plan
+        if not in_first:
+            mp.mp_token_weights_dev(w.k, cnt, wts)
         for i in range(w.k - 1):
-            mp.mp_accumulate_group(plan, [dev.gsets[i]], wts.data_ptr() + 4 * i, i == 0)
+            if in_first and i == 0:
+                mp.mp_accumulate_first_counts(plan, [dev.gsets[0]], w.k, cnt, wts)
+            else:
+                mp.mp_accumulate_group(plan, [dev.gsets[i]], wts.data_ptr() + 4 * i, i == 0)
         mp.mp_update_step_group(plan, dev.state, [dev.gsets[-1]], wts.data_ptr() + 4 * (w.k - 1),
                                 w.k == 1, w.max_norm, dev.hp)
         after = dev.stats()
@@ -122,10 +135,13 @@ def test_refused_counts_skip_the_step(mp):
         dev.close()
 
 
-def test_graph_replays_read_each_replays_counts(mp):
+@pytest.mark.parametrize("bench_graph", [False, True])
+def test_graph_replays_read_each_replays_counts(mp, bench_graph):
     """A captured step (device weights, accumulation, update) replayed with new counts written
     into the same device buffer between replays equals eager steps with host weights of those
-    counts, bit for bit, on every replay."""
+    counts, bit for bit, on every replay.  bench_graph: bench.py's captured step (the weights
+    computed inside the first accumulation, then mp_update_step_group); else
+    mp_token_weights_dev and the norm, AdamW and scaler as three calls."""
     import torch
     from harness import DeviceRun
     w = configs.make("llama-10.5M")
@@ -141,15 +157,23 @@ def test_graph_replays_read_each_replays_counts(mp):
     with torch.cuda.graph(g, stream=cap):
         st = torch.cuda.current_stream()
         plan = graphed.model.plan
-        mp.mp_token_weights_dev(k, cnt, wts, st)
+        if not bench_graph:
+            mp.mp_token_weights_dev(k, cnt, wts, st)
         for i in range(k - 1):
-            mp.mp_accumulate_group(plan, [graphed.gsets[i]], wp[i], i == 0, st)
-        # the separate norm and AdamW calls, each reading the last weight on the device
-        mp.mp_unscale_check_norm_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0,
-                                       w.max_norm, st)
-        mp.mp_adamw_step_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0, graphed.hp,
-                               st)
-        mp.mp_scaler_update(graphed.state, st)
+            if bench_graph and i == 0:
+                mp.mp_accumulate_first_counts(plan, [graphed.gsets[0]], k, cnt, wts, st)
+            else:
+                mp.mp_accumulate_group(plan, [graphed.gsets[i]], wp[i], i == 0, st)
+        if bench_graph:
+            mp.mp_update_step_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0,
+                                    w.max_norm, graphed.hp, st)
+        else:
+            # the separate norm and AdamW calls, each reading the last weight on the device
+            mp.mp_unscale_check_norm_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0,
+                                           w.max_norm, st)
+            mp.mp_adamw_step_group(plan, graphed.state, [graphed.gsets[-1]], wp[-1], 0,
+                                   graphed.hp, st)
+            mp.mp_scaler_update(graphed.state, st)
     try:
         for r in range(1, 5):
             counts = w.token_counts(r)
