@@ -139,15 +139,25 @@ __global__ __launch_bounds__(kBlock) void k_read_pattern(const float* acc, const
 {
     const int64_t c = chunk_of(blockIdx.x, gridDim.x, span);
     const int64_t base = c * kChunk;
-    float s = 0.0f;
+    // every load of the block is issued before the first is used, as in the norm pass
+    f32x4 a[2];
+    u32x2 g[2];
+    bool ok[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int64_t e = base + lane_elem(h);
-        if (!whole(e, n)) continue;
-        const f32x4 a = ld4(acc + e);
-        const u32x2 g = ld2(g16 + e);
-        s += a.x + a.y + a.z + a.w + __uint_as_float(g.x << 16) + __uint_as_float(g.y << 16);
+        ok[h] = whole(e, n);
+        if (ok[h]) {
+            a[h] = ld4(acc + e);
+            g[h] = ld2(g16 + e);
+        }
     }
+    float s = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (ok[h])
+            s += a[h].x + a[h].y + a[h].z + a[h].w + __uint_as_float(g[h].x << 16) +
+                 __uint_as_float(g[h].y << 16);
     if (s == 1.2345f) sink[blockIdx.x] = s;   // practically never: keeps the loads
 }
 
