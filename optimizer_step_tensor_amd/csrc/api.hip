@@ -194,13 +194,39 @@ int32_t pick_chunk_elems(int64_t total, int grid_cap)
     return static_cast<int32_t>(ch);
 }
 
+int32_t chunk_elems_of(int32_t n_tensors, const int64_t* numel, int cus)
+{
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) total += numel[i];
+    return pick_chunk_elems(total, cus * 8);
+}
+
+// Whether a list needs more chunks than a launch grid holds, whatever the
+// chunk size (it is at most MPK_MAX_CHUNK): checked before any table is built.
+bool too_many_chunks(int32_t n_tensors, const int64_t* numel)
+{
+    int64_t n = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        n += (numel[i] + MPK_MAX_CHUNK - 1) / MPK_MAX_CHUNK;
+        if (n > INT32_MAX) return true;
+    }
+    return false;
+}
+
+// The number of chunks build_chunks makes, without making them.
+int64_t count_chunks(int32_t n_tensors, const int64_t* numel, int cus)
+{
+    const int64_t ch = chunk_elems_of(n_tensors, numel, cus);
+    int64_t n = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) n += (numel[i] + ch - 1) / ch;
+    return n;
+}
+
 // The chunk table of a tensor list: every tensor cut into ranges of at most
 // chunk_elems elements (the last one ragged), tensor by tensor, in order.
 int32_t build_chunks(int32_t n_tensors, const int64_t* numel, int cus, std::vector<Chunk>& chunks)
 {
-    int64_t total = 0;
-    for (int32_t i = 0; i < n_tensors; ++i) total += numel[i];
-    const int32_t ch = pick_chunk_elems(total, cus * 8);
+    const int32_t ch = chunk_elems_of(n_tensors, numel, cus);
     chunks.clear();
     for (int32_t i = 0; i < n_tensors; ++i)
         for (int64_t s = 0; s < numel[i]; s += ch)
@@ -463,6 +489,8 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
             if (total > (int64_t(1) << 48))
                 return fail(MP_ERR_INVALID, "the plan holds more than 2^48 elements");
         }
+        if (too_many_chunks(n_tensors, numel))
+            return fail(MP_ERR_INVALID, "the plan needs more than 2^31 - 1 chunks");
         int device = 0;
         hipError_t e = hipGetDevice(&device);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -470,6 +498,10 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
         const int cus = device_cus(device);
         const int64_t grid_cap = MPK_ELEM_BLOCKS_PER_CU > 0 ? int64_t(cus) * MPK_ELEM_BLOCKS_PER_CU
                                                              : int64_t(1) << 30;
+        // the norm pass launches one block per chunk (or per group of chunks):
+        // refuse a chunk count beyond a launch grid before building the table
+        if (count_chunks(n_tensors, numel, cus) > INT32_MAX)
+            return fail(MP_ERR_INVALID, "the plan needs more than 2^31 - 1 chunks");
         const int32_t ch = build_chunks(n_tensors, numel, cus, chunks);
         mp_plan* p = new (std::nothrow) mp_plan();
         if (p == nullptr) return fail(MP_ERR_NOMEM, "host allocation failed");
@@ -481,7 +513,9 @@ mp_status mp_plan_create(int32_t n_tensors, const int64_t* numel, mp_dtype16 dty
         p->n_chunks = static_cast<int64_t>(chunks.size());
         p->chunk_elems = ch;
         p->grid = static_cast<int>(std::min<int64_t>(p->n_chunks, grid_cap));
-        p->norm_grid = p->grid;
+        // the accumulate and AdamW blocks stride over the chunks when the grid is
+        // capped; the norm's blocks each take a fixed chunk (or 16), never capped
+        p->norm_grid = static_cast<int>(p->n_chunks);
         p->numel.assign(numel, numel + n_tensors);
         // every partial sum is written by its block before any kernel reads it
         const size_t partial_bytes = (static_cast<size_t>(p->norm_grid) + mpk::kNormStage2) * sizeof(double);
@@ -528,6 +562,8 @@ mp_status mp_chunk_layout(int32_t n_tensors, const int64_t* numel, int32_t n_cus
         for (int32_t i = 0; i < n_tensors; ++i)
             if (numel[i] < 1 || numel[i] > (int64_t(1) << 40))
                 return fail(MP_ERR_INVALID, "tensor %d: numel out of range", i);
+        if (too_many_chunks(n_tensors, numel) || count_chunks(n_tensors, numel, n_cus) > INT32_MAX)
+            return fail(MP_ERR_INVALID, "the list needs more than 2^31 - 1 chunks");
         std::vector<Chunk> chunks;
         const int32_t ch = build_chunks(n_tensors, numel, n_cus, chunks);
         if (chunk_elems) *chunk_elems = ch;

@@ -141,6 +141,13 @@ def test_validation_before_any_device_work(mp):
     gp = ctypes.cast((ctypes.c_void_p * big_n)(*([0x10000] * big_n)), PP)
     assert L.mp_plan_create(big_n, big, 0, None, gp, gp, gp, gp, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
     assert "2^48" in mp.mp_last_error()
+    # more chunks than a launch grid holds (2^42 elements in 2048-element chunks) is refused
+    # before the chunk table is built, by the plan and by the host-only layout call
+    four = (ctypes.c_int64 * 4)(*([2 ** 40] * 4))
+    g4 = ctypes.cast((ctypes.c_void_p * 4)(*([0x10000] * 4)), PP)
+    assert L.mp_plan_create(4, four, 0, None, g4, g4, g4, g4, None, ctypes.byref(out)) == mp.MP_ERR_INVALID
+    assert "2^31" in mp.mp_last_error()
+    assert L.mp_chunk_layout(4, four, 256, None, None, None, None, None, 0) == mp.MP_ERR_INVALID
     neg = (ctypes.c_float * 1)(-1.0)
     assert L.mp_plan_create(1, ne, 0, None, g, g, g, g, neg, ctypes.byref(out)) == mp.MP_ERR_INVALID
     for cfg in (mp.scaler_cfg(init_scale=3.0), mp.scaler_cfg(growth=0.5), mp.scaler_cfg(backoff=2.0),
