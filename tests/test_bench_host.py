@@ -63,3 +63,21 @@ def test_unknown_extras_are_refused_before_any_work():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extras",
                         "resident_groups,nonsense"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and r.stdout == "" and "nonsense" in r.stderr
+
+
+def test_launches_per_step_match_the_traced_steps():
+    """The launches bench.py reports per step, against the kernels the traces of its steps show
+    (profiles/kernel_trace_*.md): the k - 1 accumulations (the token weights inside the first,
+    their own launch when k = 1), the norm's first stage, its second stage above 8192 partial
+    sums, its finish, AdamW, and the clock and the scaler unless one call folds them into the
+    finish."""
+    cases = [  # (k, chunks, eager launches, captured launches)
+        (4, 5153, 8, 6),          # llama-10.5M
+        (1, 60842, 6, 4),         # gpt-124M: one 16-bit stream, 16 chunks per norm block
+        (8, 642490, 13, 11),      # gpt-1.3B
+        (4, 328215, 9, 7),        # ragged-4096
+        (4, 3921026, 9, 7),       # llama3-8B
+    ]
+    for k, chunks, eager, captured in cases:
+        assert bench.launches_per_step(k, chunks, False) == eager, (k, chunks)
+        assert bench.launches_per_step(k, chunks, True) == captured, (k, chunks)
