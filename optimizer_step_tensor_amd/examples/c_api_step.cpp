@@ -149,6 +149,33 @@ int main()
         }
     }
     if (worst2 > 8 * std::ldexp(1.0, -25)) ++bad;
+
+    // Step 3, one micro-batch at a time with the counts still on the device: the first
+    // accumulation computes the token weights itself and leaves both in d_weights, where the
+    // folded last micro-batch reads its own (1/4 and 3/4 again: the same sum of squares and
+    // another lr * g / (g + eps) per weight).
+    HIP_OK(hipMemset(d_weights, 0, 2 * sizeof(float)));
+    MP_OK_(mp_accumulate_first_counts(plan, both, 1, 2, d_counts, d_weights, stream));
+    MP_OK_(mp_update_step_group(plan, state, both + 1, d_weights + 1, 1, 1, 0, 0.0f, &hp,
+                                stream));
+    mp_stats stats3;
+    MP_OK_(mp_state_read(state, &stats3, stream));
+    float w3[2];
+    HIP_OK(hipMemcpyAsync(w3, d_weights, sizeof w3, hipMemcpyDeviceToHost, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    if (stats3.found_inf != 0 || stats3.step != 3 || stats3.sumsq != want_sumsq) ++bad;
+    if (w3[0] != 0.25f || w3[1] != 0.75f) ++bad;
+    const double want_w3 = master0 - 3e-3 * (g / (g + 1e-8));
+    double worst3 = 0.0;
+    for (int i = 0; i < n; ++i) {
+        std::vector<float> w(numel[i]);
+        HIP_OK(hipMemcpy(w.data(), master[i], numel[i] * sizeof(float), hipMemcpyDeviceToHost));
+        for (int64_t j = 0; j < numel[i]; ++j) {
+            const double err = std::fabs(static_cast<double>(w[j]) - want_w3);
+            worst3 = err > worst3 ? err : worst3;
+        }
+    }
+    if (worst3 > 12 * std::ldexp(1.0, -25)) ++bad;
     (void)hipFree(d_counts);
     (void)hipFree(d_weights);
 
@@ -162,8 +189,8 @@ int main()
     (void)hipStreamDestroy(stream);
 
     std::printf("c_api_step: %s  params %lld  sumsq %.17g (want %.17g)  norm %.9g  "
-                "max |w - closed form| %.3g after step 1, %.3g after step 2\n",
+                "max |w - closed form| %.3g after step 1, %.3g after step 2, %.3g after step 3\n",
                 bad ? "MISMATCH" : "ok", static_cast<long long>(total), stats.sumsq, want_sumsq,
-                static_cast<double>(stats.grad_norm), worst, worst2);
+                static_cast<double>(stats.grad_norm), worst, worst2, worst3);
     return bad ? 1 : 0;
 }

@@ -1,8 +1,8 @@
 """The C ABI without PyTorch (needs a GPU): optimizer_step_tensor_amd/examples/c_api_step,
-a plain HIP program built by __graft_entry__.build(), runs two updates on hipMalloc'd buffers
+a plain HIP program built by __graft_entry__.build(), runs three updates on hipMalloc'd buffers
 (the second with token weights computed on the device and both micro-batches folded in as one
-group) and checks them against closed forms (exact sum of squares, the first two AdamW
-steps)."""
+group, the third with the weights computed inside the first accumulation) and checks them
+against closed forms (exact sum of squares, the token weights, the first three AdamW steps)."""
 import os
 import subprocess
 
