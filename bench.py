@@ -435,8 +435,12 @@ def group_bytes_per_param(acc_groups, fold):
 def time_groups(mp, torch, w, model, sets, state, hp, weights, stream, reps=3):
     """k <= 4: all micro-batches folded into the norm and AdamW passes, and (k >= 3) the first
     two accumulated in one pass with the rest folded.  k > 4: the first k - 4 accumulated in
-    groups of up to four, the last four folded."""
+    groups of up to four, the last four folded.  Each schedule is timed eagerly (host weights)
+    and as a captured step replayed (token weights computed on the device from device counts,
+    every pass reading its weights there)."""
     k = w.k
+    counts_dev = torch.tensor(w.token_counts(1), dtype=torch.int64, device="cuda")
+    wdev = torch.empty(k, dtype=torch.float32, device="cuda")
     schedules = {}
     if k <= 4:
         schedules["all_folded"] = ([], list(range(k)))
@@ -457,11 +461,29 @@ def time_groups(mp, torch, w, model, sets, state, hp, weights, stream, reps=3):
                                     stream)
         ms = time_launches(torch, stream, step, reps)
         bpp = group_bytes_per_param(acc_groups, fold)
+
+        def device_step(s):
+            mp.mp_token_weights_dev(k, counts_dev, wdev, s)
+            for i, g in enumerate(acc_groups):
+                mp.mp_accumulate_group(model.plan, [sets[j] for j in g],
+                                       wdev.data_ptr() + 4 * g[0], i == 0, s)
+            mp.mp_update_step_group(model.plan, state, [sets[j] for j in fold],
+                                    wdev.data_ptr() + 4 * fold[0], not acc_groups, w.max_norm, hp,
+                                    s)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            device_step(torch.cuda.current_stream())
+        gms = time_launches(torch, stream, graph.replay, 10 * reps)
+        del graph
         out[name] = {"schedule": {"accumulated": acc_groups, "folded": fold},
                      "bytes_per_param": bpp, "ms_per_step": ms,
                      "params_per_s": w.total / (ms * 1e-3),
                      "GBps": bpp * w.total / ms / 1e6,
-                     "frac": bpp * w.total / ms / 1e6 / HBM_PEAK_GBPS}
+                     "frac": bpp * w.total / ms / 1e6 / HBM_PEAK_GBPS,
+                     "graph_ms_per_step": gms,
+                     "graph_frac": bpp * w.total / gms / 1e6 / HBM_PEAK_GBPS}
     return out
 
 
