@@ -32,7 +32,7 @@
  *  [TS]  "Chapter 41 Training at Scale": section 41.1, equation (41.1);
  *        section 41.5, fine-grained FP8 scaling (listing 41.5).
  *
- * Readings where the pages are silent (each one is listed in the design notes):
+ * Readings where the pages are silent, ambiguous or leave a detail open:
  *  - AdamW: the pages describe it only in words ([ZQ]); the per-element
  *    sequence in or_adamw_tensor is the standard decoupled AdamW with the bias
  *    corrections applied to m and v, epsilon added after the square root, and
