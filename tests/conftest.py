@@ -16,20 +16,20 @@ def pytest_configure(config):
 @pytest.fixture
 def progress(capsys):
     """A progress printer for long tests: each line goes past pytest's capture to the real
-    stdout (flushed) and into gpurun_out/test_progress.log, so that a long test is seen to
-    be alive while it runs."""
-    log_dir = os.path.join(ROOT, "gpurun_out")
+    stdout (flushed), and is appended to the file MPSTEP_PROGRESS_LOG names, if set, so that
+    a long test is seen to be alive while it runs."""
+    log = os.environ.get("MPSTEP_PROGRESS_LOG")
 
     def say(*a):
         line = " ".join(str(x) for x in a)
         with capsys.disabled():
             print(line, flush=True)
-        try:
-            os.makedirs(log_dir, exist_ok=True)
-            with open(os.path.join(log_dir, "test_progress.log"), "a") as f:
-                f.write(line + "\n")
-        except OSError:
-            pass
+        if log:
+            try:
+                with open(log, "a") as f:
+                    f.write(line + "\n")
+            except OSError:
+                pass
     return say
 
 
